@@ -1,0 +1,211 @@
+#!/usr/bin/env python
+"""Benchmark: one d20-shaped GPT block training step (forward + backward) on
+one MI355X, B=4, T=2048, width 1280, 10 heads x 128, RMSNorm, RoPE, QK-norm.
+
+Prints one JSON line: tokens/s of the step, the roofline of the dominant
+kernel (timed with hipEvents on the library's stream during a traced pass of
+the same steps), and the float64 CPU oracle timed on a bounded sample of the
+same workload.  Inputs are seeded synthetic tensors resident in HBM before
+the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "train tokens/s (fwd+bwd) on 1 GPU, d20 shape; % bf16 MFMA peak"
+PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
+
+
+def block_flops(B, T, C, H):
+    """Useful FLOPs of one block fwd+bwd: 6 * 12 C^2 per token for the
+    Linear layers, causal attention counted on the lower triangle."""
+    D = C // H
+    N = B * T
+    lin = 6 * 12 * C * C * N
+    attn_fwd = 2 * B * H * D * T * T        # QK^T and PV, each 2*B*H*D*T^2/2
+    return lin + 3 * attn_fwd                 # backward = 2x forward
+
+
+def site_work(name, B, T, C, H):
+    """(bound, algorithmic work per launch) of a block call site."""
+    N, D = B * T, C // H
+    g = lambda m, n, k: 2.0 * m * n * k  # noqa: E731
+    half = B * H * D * T * T                 # one causal T x T x D product (2*T^2*D/2 per head)
+    flops = {
+        "qkv_gemm": g(N, 3 * C, C), "qkv_dgrad": g(N, C, 3 * C), "qkv_wgrad": g(3 * C, C, N),
+        "out_gemm": g(N, C, C), "out_dgrad": g(N, C, C), "out_wgrad": g(C, C, N),
+        "fc_gemm_gelu": g(N, 4 * C, C), "fc_dgrad": g(N, C, 4 * C), "fc_wgrad": g(4 * C, C, N),
+        "proj_gemm": g(N, C, 4 * C), "proj_dgrad_gelu": g(N, 4 * C, C), "proj_wgrad": g(C, 4 * C, N),
+        "attn_fwd": 2 * half, "attn_bwd_dkdv": 3 * half, "attn_bwd_dq": 1 * half,
+    }
+    if name in flops:
+        return "mfma", flops[name]
+    s = 2  # bf16
+    bytes_ = {
+        "norm1_fwd": N * C * 2 * s + 8 * N, "norm2_fwd": N * C * 2 * s + 8 * N,
+        "norm1_bwd": N * C * 4 * s, "norm2_bwd": N * C * 4 * s,
+        "qk_rope_norm": 2 * N * 2 * C * s, "qk_bwd": 3 * N * 2 * C * s,
+        "attn_delta": 2 * N * C * s + 4 * N * H,
+    }
+    if name in bytes_:
+        return "hbm", bytes_[name]
+    return None, None
+
+
+def cpu_baseline(w, budget_s=30.0):
+    """The float64 oracle on one sequence of the workload (B=1 of 4)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    import oracle as O
+    from decoder_only_gpt_bf16_amd import synth
+    ws = synth.scaled(w, B=1)
+    x, dy, p = synth.make_block_inputs(ws)
+    cfg = synth.oracle_cfg(ws.cfg)
+    t0 = time.perf_counter()
+    y, cache = O.block_fwd(cfg, x, p)
+    O.block_bwd(cfg, dy, cache, p)
+    dt = time.perf_counter() - t0
+    return {"value": ws.B * ws.T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one sequence (B=1, T={ws.T}) of the d20 block fwd+bwd in float64 NumPy, {dt:.1f} s"}
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time the GPT-2 block, GPT-2 step and d20 eval")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import BlockRunner
+
+    w = synth.D20_BLOCK
+    cfg = w.cfg
+    x, dy, p = synth.make_block_inputs(w)
+    r = BlockRunner(cfg, w.B, w.T, x, dy, p)
+    torch.cuda.synchronize()
+    ms = time_steps(r.step, args.steps, args.warmup)
+    flops = block_flops(w.B, w.T, cfg.n_embd, cfg.n_head)
+    tok_s = w.B * w.T / (ms * 1e-3)
+
+    # traced pass over the same number of steps: per call-site kernel times
+    B.gpt_trace_begin(64 * args.steps)
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    trace = B.gpt_trace_end()
+    sites = {}
+    for name, (n, us) in trace.items():
+        bound, work = site_work(name, w.B, w.T, cfg.n_embd, cfg.n_head)
+        avg = us / n
+        e = {"launches_per_step": n / args.steps, "avg_us": round(avg, 2), "share": 0.0}
+        if bound:
+            e["bound"] = bound
+            e["frac"] = (work / (avg * 1e-6)) / (PEAK_BF16 if bound == "mfma" else PEAK_HBM)
+        sites[name] = e
+    total_us = sum(us for _, us in trace.values())
+    for name, (n, us) in trace.items():
+        sites[name]["share"] = round(us / total_us, 4)
+    dom = max((k for k in trace if site_work(k, w.B, w.T, cfg.n_embd, cfg.n_head)[0]), key=lambda k: trace[k][1])
+    bound, work = site_work(dom, w.B, w.T, cfg.n_embd, cfg.n_head)
+    n, us = trace[dom]
+    avg_s = us / n * 1e-6
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": work / avg_s / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_us"] = round(us / n, 2)
+    roof["work_per_launch"] = work
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "d20 block fwd+bwd (RMSNorm, RoPE, QK-norm, GELU MLP)", "batch": w.B, "seq_len": w.T,
+                   "n_embd": cfg.n_embd, "n_head": cfg.n_head, "head_dim": cfg.head_dim},
+        "mfma_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4),
+        "flop_per_step": flops,
+        "roofline": roof,
+        "kernels": sites,
+    }
+    if args.extra:
+        out["extra"] = extra_workloads(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+def extra_workloads(args):
+    import torch
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import BlockRunner, ModelRunner
+    res = {}
+    w = synth.GPT2_BLOCK
+    x, dy, p = synth.make_block_inputs(w)
+    r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
+    ms = time_steps(r.step, args.steps, args.warmup)
+    f = block_flops(w.B, w.T, w.cfg.n_embd, w.cfg.n_head)
+    res[w.name] = {"tokens_per_s": w.B * w.T / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16}
+    del r
+    w = synth.GPT2_STEP
+    ids, y, P, tb = synth.make_model_inputs(w)
+    m = ModelRunner(w.cfg, w.B, w.T, P, tb)
+    m.set_batch(ids, y)
+    ms = time_steps(m.train_step, max(3, args.steps // 4), 2)
+    C, L, V, N = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T
+    f = L * block_flops(w.B, w.T, C, w.cfg.n_head) + 6.0 * N * C * V
+    res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
+                   "loss": m.loss.item()}
+    del m
+    torch.cuda.empty_cache()
+    w = synth.D20_EVAL
+    ids, y, P, tb = synth.make_model_inputs(w)
+    m = ModelRunner(w.cfg, w.B, w.T, P, tb, train=False)
+    m.set_batch(ids, y)
+    ms = time_steps(m.eval_step, max(3, args.steps // 4), 2)
+    C, L, V, N, T = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T, w.T
+    f = L * (2 * 12 * C * C * N + 2 * w.B * w.cfg.n_head * (C // w.cfg.n_head) * T * T) + 2.0 * N * C * V
+    res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
+                   "bpb": m.sum_nats.item() / (math.log(2) * m.sum_bytes.item())}
+    return res
+
+
+if __name__ == "__main__":
+    main()

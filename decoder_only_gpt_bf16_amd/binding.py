@@ -1,0 +1,197 @@
+"""ctypes binding of libgptmi.so: the C entry points under the same names.
+
+Argument marshalling only: torch tensors become device pointers, the current
+torch stream becomes the hipStream_t argument, status codes become
+exceptions.  Every computation runs in the library's HIP kernels.  Loading
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptmi.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gptmi.h")
+
+GPT_OK, GPT_ERR_INVALID, GPT_ERR_UNSUPPORTED, GPT_ERR_WORKSPACE, GPT_ERR_HIP = range(5)
+BLOCK_FIELDS = ("ln1_w", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
+                "ln2_w", "ln2_b", "w_fc", "b_fc", "w_proj", "b_proj")
+
+
+class GptError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gptmi status {status}: {msg}")
+        self.status = status
+
+
+class GptConfigC(ctypes.Structure):
+    _fields_ = [("n_layer", ctypes.c_int32), ("n_head", ctypes.c_int32), ("n_embd", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("vocab_size", ctypes.c_int32), ("bias", ctypes.c_int32),
+                ("norm", ctypes.c_int32), ("rope", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class BlockWeightsC(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in BLOCK_FIELDS]
+
+
+class BlockGradsC(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in BLOCK_FIELDS]
+
+
+_lib = None
+_VP, _I, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+_CFG = ctypes.POINTER(GptConfigC)
+
+_SIGS = {
+    "gpt_block_saved_bytes": (_SZ, [_CFG, _I, _I]),
+    "gpt_workspace_bytes": (_SZ, [_CFG, _I, _I]),
+    "gpt_block_fwd": (_I, [_CFG, _I, _I, _VP, ctypes.POINTER(BlockWeightsC), _VP, _VP, _VP, _SZ, _VP]),
+    "gpt_block_bwd": (_I, [_CFG, _I, _I, _VP, _VP, ctypes.POINTER(BlockWeightsC), _VP, _VP,
+                           ctypes.POINTER(BlockGradsC), _I, _VP, _SZ, _VP]),
+    "lm_head_xent_fwd_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "val_bpb_reduce": (_I, [_I, _VP, _VP, _VP, _I, _VP, _VP, _VP]),
+    "gpt_embed_fwd": (_I, [_CFG, _I, _I, _VP, _VP, _VP, _VP, _VP]),
+    "gpt_embed_bwd": (_I, [_CFG, _I, _I, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "gpt_norm_fwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "gpt_norm_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "gpt_trace_begin": (_I, [_I]),
+    "gpt_trace_end": (_I, [ctypes.c_char_p, _SZ]),
+    "gpt_status_string": (ctypes.c_char_p, [_I]),
+    "gpt_last_error": (ctypes.c_char_p, []),
+}
+
+
+def header_functions() -> list:
+    """Names of the functions include/gptmi.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "sizeof"})
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgptmi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decoder_only_gpt_bf16_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def make_config(cfg) -> GptConfigC:
+    """From a synth.GPTConfig-like object."""
+    return GptConfigC(cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size, cfg.vocab_size, int(cfg.bias),
+                      0 if cfg.norm == "layernorm" else 1, int(cfg.rope), int(cfg.qk_norm),
+                      float(cfg.rope_base), float(cfg.eps), 1 if cfg.dtype == "bf16" else 0)
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to gptmi must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check(status: int):
+    if status != GPT_OK:
+        raise GptError(status, lib().gpt_last_error().decode())
+
+
+def _block_struct(cls, d: dict):
+    return cls(*[_p(d.get(f)) for f in BLOCK_FIELDS])
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def gpt_block_saved_bytes(cfg: GptConfigC, B: int, T: int) -> int:
+    return lib().gpt_block_saved_bytes(ctypes.byref(cfg), B, T)
+
+
+def gpt_workspace_bytes(cfg: GptConfigC, B: int, T: int) -> int:
+    return lib().gpt_workspace_bytes(ctypes.byref(cfg), B, T)
+
+
+def gpt_block_fwd(cfg, B, T, x, w: dict, y, saved, ws, stream=None):
+    W = _block_struct(BlockWeightsC, w)
+    _check(lib().gpt_block_fwd(ctypes.byref(cfg), B, T, _p(x), ctypes.byref(W), _p(y), _p(saved), _p(ws),
+                               _nbytes(ws), _stream(stream)))
+
+
+def gpt_block_bwd(cfg, B, T, x, dy, w: dict, saved, dx, grads: dict, accumulate, ws, stream=None):
+    W = _block_struct(BlockWeightsC, w)
+    G = _block_struct(BlockGradsC, grads)
+    _check(lib().gpt_block_bwd(ctypes.byref(cfg), B, T, _p(x), _p(dy), ctypes.byref(W), _p(saved), _p(dx),
+                               ctypes.byref(G), int(accumulate), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def lm_head_xent_fwd_bwd(cfg, N, h, W, targets, loss_scale, loss, nats, dh, dW, accumulate, ws, stream=None):
+    _check(lib().lm_head_xent_fwd_bwd(ctypes.byref(cfg), N, _p(h), _p(W), _p(targets), float(loss_scale), _p(loss),
+                                      _p(nats), _p(dh), _p(dW), int(accumulate), _p(ws), _nbytes(ws),
+                                      _stream(stream)))
+
+
+def val_bpb_reduce(N, nats, targets, token_bytes, V, sum_nats, sum_bytes, stream=None):
+    _check(lib().val_bpb_reduce(N, _p(nats), _p(targets), _p(token_bytes), V, _p(sum_nats), _p(sum_bytes),
+                                _stream(stream)))
+
+
+def gpt_embed_fwd(cfg, B, T, ids, wte, wpe, x0, stream=None):
+    _check(lib().gpt_embed_fwd(ctypes.byref(cfg), B, T, _p(ids), _p(wte), _p(wpe), _p(x0), _stream(stream)))
+
+
+def gpt_embed_bwd(cfg, B, T, ids, dx0, dwte, dwpe, accumulate, ws, stream=None):
+    _check(lib().gpt_embed_bwd(ctypes.byref(cfg), B, T, _p(ids), _p(dx0), _p(dwte), _p(dwpe), int(accumulate),
+                               _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def gpt_trace_begin(capacity: int):
+    _check(lib().gpt_trace_begin(capacity))
+
+
+def gpt_trace_end() -> dict:
+    """{call-site name: (launches, total microseconds)}."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(lib().gpt_trace_end(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, us = line.split()
+        out[name] = (int(n), float(us))
+    return out
+
+
+def gpt_norm_fwd(cfg, N, x, w, b, y, stats, stream=None):
+    _check(lib().gpt_norm_fwd(ctypes.byref(cfg), N, _p(x), _p(w), _p(b), _p(y), _p(stats), _stream(stream)))
+
+
+def gpt_norm_bwd(cfg, N, x, w, dy, resid, dx, dw, db, accumulate, ws, stream=None):
+    _check(lib().gpt_norm_bwd(ctypes.byref(cfg), N, _p(x), _p(w), _p(dy), _p(resid), _p(dx), _p(dw), _p(db),
+                              int(accumulate), _p(ws), _nbytes(ws), _stream(stream)))

@@ -1,0 +1,645 @@
+// C ABI of the library (declared in include/gptmi.h): argument validation,
+// saved-activation and workspace planning, and the launch sequence of each
+// entry point on the caller's stream.  No allocation, no synchronisation.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gptmi.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(call)                                                                       \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(GPT_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+// Optional per-call-site timing: a pair of events recorded on the call's
+// stream around each kernel call site, from a pool created by
+// gpt_trace_begin (diagnostics only; off by default).
+struct TraceState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<const char*, size_t>> recs;  // name, first event index
+} g_trace;
+
+struct TraceScope {
+  hipStream_t s;
+  const char* name;
+  long idx = -1;
+  TraceScope(const char* n, hipStream_t st) : s(st), name(n) {
+    if (!g_trace.on) return;
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    if (g_trace.used + 2 > g_trace.pool.size()) return;
+    idx = (long)g_trace.used;
+    g_trace.used += 2;
+    (void)hipEventRecord(g_trace.pool[idx], s);
+  }
+  ~TraceScope() {
+    if (idx < 0) return;
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    (void)hipEventRecord(g_trace.pool[idx + 1], s);
+    g_trace.recs.emplace_back(name, (size_t)idx);
+  }
+};
+
+// Launch a kernel call site under a name (timed when tracing is on).
+#define RUN(name, call)                  \
+  do {                                   \
+    TraceScope ts_(name, s);             \
+    HIPCHK(call);                        \
+  } while (0)
+
+// Sequential 256-byte aligned carving of a buffer; with base == nullptr it
+// only measures.
+struct Arena {
+  char* base;
+  size_t off = 0;
+  explicit Arena(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = align256(off);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+  template <typename T> T* take_n(size_t n) { return static_cast<T*>(take(n * sizeof(T))); }
+  size_t used() const { return align256(off); }
+};
+
+struct Dims {
+  int B, T, N, C, H, D, V, dtype;
+  size_t es;  // storage element size
+};
+
+int check_cfg(const gpt_config* cfg, Dims& d) {
+  if (!cfg) return fail(GPT_ERR_INVALID, "cfg is NULL");
+  if (cfg->n_head <= 0 || cfg->n_embd <= 0 || cfg->block_size <= 0 || cfg->vocab_size <= 0)
+    return fail(GPT_ERR_INVALID, "non-positive n_head/n_embd/block_size/vocab_size");
+  if (cfg->n_embd % cfg->n_head) return fail(GPT_ERR_INVALID, "n_embd %% n_head != 0");
+  if (cfg->dtype != GPT_DTYPE_FP32 && cfg->dtype != GPT_DTYPE_BF16)
+    return fail(GPT_ERR_UNSUPPORTED, "unknown dtype %d", cfg->dtype);
+  if (cfg->norm != GPT_NORM_LAYERNORM && cfg->norm != GPT_NORM_RMSNORM)
+    return fail(GPT_ERR_INVALID, "unknown norm %d", cfg->norm);
+  if (!(cfg->norm_eps >= 0.0f)) return fail(GPT_ERR_INVALID, "norm_eps must be >= 0");
+  d.C = cfg->n_embd;
+  d.H = cfg->n_head;
+  d.D = d.C / d.H;
+  d.V = cfg->vocab_size;
+  d.dtype = cfg->dtype;
+  d.es = cfg->dtype == GPT_DTYPE_BF16 ? 2 : 4;
+  if (cfg->rope && (d.D & 1)) return fail(GPT_ERR_INVALID, "odd head_dim %d with rope", d.D);
+  if (cfg->rope && !(cfg->rope_base > 0.0f)) return fail(GPT_ERR_INVALID, "rope_base must be > 0");
+  if (d.D % 8 || d.D > 128) return fail(GPT_ERR_UNSUPPORTED, "head_dim %d not a multiple of 8 in [8, 128]", d.D);
+  if (d.C > 2048) return fail(GPT_ERR_UNSUPPORTED, "n_embd %d > 2048", d.C);
+  return GPT_OK;
+}
+
+int check_bt(const gpt_config* cfg, int B, int T, Dims& d) {
+  int st = check_cfg(cfg, d);
+  if (st) return st;
+  if (B <= 0 || T <= 0) return fail(GPT_ERR_INVALID, "B and T must be positive (B=%d T=%d)", B, T);
+  if (T > cfg->block_size) return fail(GPT_ERR_INVALID, "T=%d exceeds block_size=%d", T, cfg->block_size);
+  if ((long)B * T * 4L * cfg->n_embd >= (1L << 31) * 8L) return fail(GPT_ERR_UNSUPPORTED, "batch too large");
+  d.B = B;
+  d.T = T;
+  d.N = B * T;
+  return GPT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ------------------------------------------------------------ block layouts
+struct Saved {
+  void *a1, *qkv, *o, *x1, *a2, *u, *g;
+  float *stats1, *stats2, *qkr, *lse;
+};
+
+Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
+  Saved s{};
+  const size_t N = d.N, C = d.C, es = d.es;
+  s.a1 = a.take(N * C * es);
+  s.stats1 = a.take_n<float>(2 * N);
+  s.qkv = a.take(N * 3 * C * es);
+  s.qkr = cfg->qk_norm ? a.take_n<float>(2 * N * d.H) : nullptr;
+  s.o = a.take(N * C * es);
+  s.lse = a.take_n<float>((size_t)d.B * d.H * d.T);
+  s.x1 = a.take(N * C * es);
+  s.a2 = a.take(N * C * es);
+  s.stats2 = a.take_n<float>(2 * N);
+  s.u = a.take(N * 4 * C * es);
+  s.g = a.take(N * 4 * C * es);
+  return s;
+}
+
+struct BwdWs {
+  float2* cs;
+  void *du, *da, *dx1, *dO, *dqkv;
+  float *delta, *colpart, *colsum, *split;
+};
+
+GemmDesc gemm0() {
+  GemmDesc g;
+  memset(&g, 0, sizeof g);
+  return g;
+}
+
+// forward Linear: out[N, Nout] = act[N, K] W[Nout, K]^T
+GemmDesc lin_fwd(const Dims& d, const void* act, int K, const void* W, int Nout, int epi) {
+  GemmDesc g = gemm0();
+  g.A = act; g.lda = K; g.a_kmaj = false;
+  g.B = W; g.ldb = K; g.b_kmaj = false;
+  g.M = d.N; g.N = Nout; g.K = K; g.epi = epi;
+  return g;
+}
+// input gradient: dX[N, In] = dY[N, Out] W[Out, In]
+GemmDesc lin_dgrad(const Dims& d, const void* dY, int Out, const void* W, int In, int epi) {
+  GemmDesc g = gemm0();
+  g.A = dY; g.lda = Out; g.a_kmaj = false;
+  g.B = W; g.ldb = In; g.b_kmaj = true;
+  g.M = d.N; g.N = In; g.K = Out; g.epi = epi;
+  return g;
+}
+// weight gradient: dW[Out, In] (+)= dY[N, Out]^T X[N, In]
+GemmDesc lin_wgrad(const Dims& d, const void* dY, int Out, const void* X, int In, float* dW, int accumulate) {
+  GemmDesc g = gemm0();
+  g.A = dY; g.lda = Out; g.a_kmaj = true;
+  g.B = X; g.ldb = In; g.b_kmaj = true;
+  g.M = Out; g.N = In; g.K = d.N; g.epi = EPI_F32;
+  g.out = dW; g.ldc = In; g.accumulate = accumulate;
+  return g;
+}
+
+size_t split_need(const Dims& d) {
+  const size_t C = d.C;
+  size_t m = 0;
+  GemmDesc g;
+  g = lin_wgrad(d, nullptr, C, nullptr, 4 * C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
+  g = lin_wgrad(d, nullptr, 4 * C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
+  g = lin_wgrad(d, nullptr, C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
+  g = lin_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
+  return m;
+}
+
+BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
+  BwdWs w{};
+  const size_t N = d.N, C = d.C, es = d.es;
+  w.cs = cfg->rope ? a.take_n<float2>((size_t)d.T * (d.D / 2)) : nullptr;
+  w.du = a.take(N * 4 * C * es);
+  w.da = a.take(N * C * es);
+  w.dx1 = a.take(N * C * es);
+  w.dO = a.take(N * C * es);
+  w.dqkv = a.take(N * 3 * C * es);
+  w.delta = a.take_n<float>((size_t)d.B * d.H * d.T);
+  w.colpart = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
+  w.colsum = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, 4 * C)));
+  w.split = static_cast<float*>(a.take(split_need(d)));
+  return w;
+}
+
+size_t fwd_ws_bytes(const Dims& d, const gpt_config* cfg, bool inference) {
+  Arena a(nullptr);
+  if (cfg->rope) a.take_n<float2>((size_t)d.T * (d.D / 2));
+  if (inference) saved_layout(d, cfg, a);
+  return a.used();
+}
+
+// ------------------------------------------------------------ LM head layout
+struct XentWs {
+  int Vc, nchunk, P;
+  long ldz;
+  float2* part;
+  float *ztgt, *lse, *nats, *loss_part, *dh_acc, *zbuf, *split;
+  float2* run;
+  void* dz;
+};
+
+constexpr int XENT_CHUNK = 8192;
+
+XentWs xent_layout(const Dims& d, int N, Arena& a) {
+  XentWs x{};
+  const int V = d.V;
+  x.Vc = std::min(V, XENT_CHUNK);
+  x.nchunk = cdiv(V, x.Vc);
+  x.ldz = (x.Vc + 7) / 8 * 8;
+  int P = 0;
+  for (int c = 0; c < x.nchunk; ++c) {
+    const int w = std::min(x.Vc, V - c * x.Vc);
+    P += 2 * cdiv(w, 256);
+  }
+  x.P = P;
+  const bool mfma = d.dtype == 1;
+  x.part = mfma ? a.take_n<float2>((size_t)N * P) : nullptr;
+  x.run = mfma ? nullptr : a.take_n<float2>((size_t)N);
+  x.ztgt = a.take_n<float>(N);
+  x.lse = a.take_n<float>(N);
+  x.nats = a.take_n<float>(N);
+  x.loss_part = a.take_n<float>(xent_finish_blocks(N));
+  x.dz = a.take((size_t)N * x.ldz * d.es);
+  x.zbuf = mfma ? nullptr : a.take_n<float>((size_t)N * x.ldz);
+  x.dh_acc = a.take_n<float>((size_t)N * d.C);
+  size_t split = 0;
+  for (int c = 0; c < x.nchunk; ++c) {
+    const int w = std::min(x.Vc, V - c * x.Vc);
+    GemmDesc g = gemm0();  // dW chunk = dz^T h
+    g.M = w; g.N = d.C; g.K = N; g.epi = EPI_F32; g.a_kmaj = true; g.b_kmaj = true;
+    GemmDesc q = gemm0();  // dh += dz W_chunk
+    q.M = N; q.N = d.C; q.K = w; q.epi = EPI_F32; q.b_kmaj = true;
+    split = std::max(split, std::max(gemm_split_scratch_bytes(g, d.dtype), gemm_split_scratch_bytes(q, d.dtype)));
+  }
+  x.split = static_cast<float*>(a.take(split));
+  return x;
+}
+
+size_t xent_ws_bytes(const Dims& d, int N) {
+  Arena a(nullptr);
+  xent_layout(d, N, a);
+  return a.used();
+}
+
+size_t embed_ws_bytes(const Dims& d) { return align256(embed_bwd_scratch_bytes(d.N, d.V)); }
+
+size_t norm_ws_bytes(const Dims& d) { return align256(2 * (size_t)norm_bwd_blocks(d.N) * d.C * sizeof(float)); }
+
+int check_block_weights(const gpt_config* cfg, const gpt_block_weights* w) {
+  if (!w) return fail(GPT_ERR_INVALID, "weights struct is NULL");
+  if (!w->w_qkv || !w->w_o || !w->w_fc || !w->w_proj) return fail(GPT_ERR_INVALID, "a Linear weight is NULL");
+  if (cfg->norm == GPT_NORM_LAYERNORM && (!w->ln1_w || !w->ln2_w))
+    return fail(GPT_ERR_INVALID, "LayerNorm gain is NULL");
+  if (cfg->bias) {
+    if (!w->b_qkv || !w->b_o || !w->b_fc || !w->b_proj) return fail(GPT_ERR_INVALID, "a Linear bias is NULL");
+    if (cfg->norm == GPT_NORM_LAYERNORM && (!w->ln1_b || !w->ln2_b))
+      return fail(GPT_ERR_INVALID, "LayerNorm bias is NULL");
+  }
+  const void* ps[] = {w->ln1_w, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o, w->b_o,
+                      w->ln2_w, w->ln2_b, w->w_fc, w->b_fc, w->w_proj, w->b_proj};
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return fail(GPT_ERR_INVALID, "weight pointer not 16-byte aligned");
+  return GPT_OK;
+}
+
+const void* opt(const gpt_config* cfg, const void* p) { return cfg->bias ? p : nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt_status_string(int status) {
+  switch (status) {
+    case GPT_OK: return "ok";
+    case GPT_ERR_INVALID: return "invalid argument";
+    case GPT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GPT_ERR_WORKSPACE: return "workspace too small";
+    case GPT_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gpt_last_error(void) { return g_err.c_str(); }
+
+int gpt_trace_begin(int capacity) {
+  if (capacity <= 0) return fail(GPT_ERR_INVALID, "capacity must be positive");
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  while (g_trace.pool.size() < 2 * (size_t)capacity) {
+    hipEvent_t e;
+    HIPCHK(hipEventCreate(&e));
+    g_trace.pool.push_back(e);
+  }
+  g_trace.used = 0;
+  g_trace.recs.clear();
+  g_trace.on = true;
+  return GPT_OK;
+}
+
+int gpt_trace_end(char* buf, size_t len) {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  g_trace.on = false;
+  std::map<std::string, std::pair<long, double>> agg;
+  std::vector<std::string> order;
+  for (auto& r : g_trace.recs) {
+    HIPCHK(hipEventSynchronize(g_trace.pool[r.second + 1]));
+    float ms = 0.0f;
+    HIPCHK(hipEventElapsedTime(&ms, g_trace.pool[r.second], g_trace.pool[r.second + 1]));
+    auto it = agg.find(r.first);
+    if (it == agg.end()) { order.push_back(r.first); agg[r.first] = {1, ms * 1000.0}; }
+    else { it->second.first += 1; it->second.second += ms * 1000.0; }
+  }
+  std::string out;
+  char line[160];
+  for (auto& n : order) {
+    snprintf(line, sizeof line, "%s %ld %.3f\n", n.c_str(), agg[n].first, agg[n].second);
+    out += line;
+  }
+  g_trace.recs.clear();
+  g_trace.used = 0;
+  if (buf && len) {
+    strncpy(buf, out.c_str(), len - 1);
+    buf[len - 1] = 0;
+  }
+  if (out.size() + 1 > len) return fail(GPT_ERR_INVALID, "trace buffer too small (%zu bytes needed)", out.size() + 1);
+  return GPT_OK;
+}
+
+size_t gpt_block_saved_bytes(const gpt_config* cfg, int B, int T) {
+  Dims d;
+  if (check_bt(cfg, B, T, d)) return 0;
+  Arena a(nullptr);
+  saved_layout(d, cfg, a);
+  return a.used();
+}
+
+size_t gpt_workspace_bytes(const gpt_config* cfg, int B, int T) {
+  Dims d;
+  if (check_bt(cfg, B, T, d)) return 0;
+  size_t m = fwd_ws_bytes(d, cfg, true);
+  Arena a(nullptr);
+  bwd_layout(d, cfg, a);
+  m = std::max(m, a.used());
+  m = std::max(m, xent_ws_bytes(d, d.N));
+  m = std::max(m, embed_ws_bytes(d));
+  m = std::max(m, norm_ws_bytes(d));
+  return m;
+}
+
+int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_block_weights* w, void* y,
+                  void* saved, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_bt(cfg, B, T, d);
+  if (st) return st;
+  if ((st = check_block_weights(cfg, w))) return st;
+  if (!x || !y) return fail(GPT_ERR_INVALID, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(saved) || !aligned16(ws))
+    return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
+  const size_t need = fwd_ws_bytes(d, cfg, saved == nullptr);
+  if (need && (!ws || ws_bytes < need))
+    return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Arena wa(ws);
+  float2* cs = cfg->rope ? wa.take_n<float2>((size_t)T * (d.D / 2)) : nullptr;
+  Arena sa(saved ? saved : wa.take(0));  // inference: intermediates follow the table
+  Saved sv = saved_layout(d, cfg, sa);
+  const int C = d.C, ty = d.dtype, kind = cfg->norm;
+
+  if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, cs, s));
+  RUN("norm1_fwd", launch_norm_fwd(ty, kind, d.N, C, x, w->ln1_w, opt(cfg, w->ln1_b), cfg->norm_eps, sv.a1, sv.stats1, s));
+  GemmDesc g = lin_fwd(d, sv.a1, C, w->w_qkv, 3 * C, EPI_STORE);
+  g.out = sv.qkv; g.ldc = 3 * C; g.bias = opt(cfg, w->b_qkv);
+  RUN("qkv_gemm", launch_gemm(g, ty, nullptr, s));
+  if (cfg->rope || cfg->qk_norm)
+    RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
+  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, sv.qkv, sv.o, sv.lse, s));
+  g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
+  g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
+  RUN("out_gemm", launch_gemm(g, ty, nullptr, s));
+  RUN("norm2_fwd", launch_norm_fwd(ty, kind, d.N, C, sv.x1, w->ln2_w, opt(cfg, w->ln2_b), cfg->norm_eps, sv.a2, sv.stats2, s));
+  g = lin_fwd(d, sv.a2, C, w->w_fc, 4 * C, EPI_GELU);
+  g.out = sv.u; g.out2 = sv.g; g.ldc = 4 * C; g.bias = opt(cfg, w->b_fc);
+  RUN("fc_gemm_gelu", launch_gemm(g, ty, nullptr, s));
+  g = lin_fwd(d, sv.g, 4 * C, w->w_proj, C, EPI_STORE);
+  g.out = y; g.ldc = C; g.bias = opt(cfg, w->b_proj); g.resid = sv.x1; g.ldr = C;
+  RUN("proj_gemm", launch_gemm(g, ty, nullptr, s));
+  return GPT_OK;
+}
+
+int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void* dy, const gpt_block_weights* w,
+                  const void* saved, void* dx, const gpt_block_grads* gr, int accumulate, void* ws,
+                  size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_bt(cfg, B, T, d);
+  if (st) return st;
+  if ((st = check_block_weights(cfg, w))) return st;
+  if (!x || !dy || !saved || !dx || !gr) return fail(GPT_ERR_INVALID, "x, dy, saved, dx or grads is NULL");
+  if (!gr->w_qkv || !gr->w_o || !gr->w_fc || !gr->w_proj) return fail(GPT_ERR_INVALID, "a weight gradient is NULL");
+  if (cfg->norm == GPT_NORM_LAYERNORM && (!gr->ln1_w || !gr->ln2_w))
+    return fail(GPT_ERR_INVALID, "LayerNorm gain gradient is NULL");
+  if (cfg->bias && (!gr->b_qkv || !gr->b_o || !gr->b_fc || !gr->b_proj ||
+                    (cfg->norm == GPT_NORM_LAYERNORM && (!gr->ln1_b || !gr->ln2_b))))
+    return fail(GPT_ERR_INVALID, "a bias gradient is NULL");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(saved) || !aligned16(dx) || !aligned16(ws))
+    return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
+  Arena probe(nullptr);
+  bwd_layout(d, cfg, probe);
+  if (!ws || ws_bytes < probe.used())
+    return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, probe.used());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Arena sa(const_cast<void*>(saved));
+  Saved sv = saved_layout(d, cfg, sa);
+  Arena wa(ws);
+  BwdWs b = bwd_layout(d, cfg, wa);
+  const int C = d.C, ty = d.dtype, kind = cfg->norm, N = d.N;
+  const int nblk = norm_bwd_blocks(N);
+  const bool ln = kind == GPT_NORM_LAYERNORM;
+
+  if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, b.cs, s));
+  // MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
+  GemmDesc g = lin_dgrad(d, dy, C, w->w_proj, 4 * C, EPI_GELU_BWD);
+  g.out = b.du; g.ldc = 4 * C; g.aux = sv.u; g.ldaux = 4 * C;
+  RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
+  RUN("proj_wgrad", launch_gemm(lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate), ty, b.split, s));
+  if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
+  g = lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
+  g.out = b.da; g.ldc = C;
+  RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
+  RUN("fc_wgrad", launch_gemm(lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate), ty, b.split, s));
+  if (cfg->bias) RUN("fc_bias", launch_colsum(ty, N, 4 * C, 4 * C, b.du, gr->b_fc, accumulate, b.colsum, s));
+  // norm 2 backward + residual
+  RUN("norm2_bwd", launch_norm_bwd(ty, kind, N, C, sv.x1, w->ln2_w, b.da, dy, cfg->norm_eps, b.dx1, b.colpart, ln, s));
+  if (ln) {
+    RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln2_w, accumulate, s));
+    if (cfg->bias) RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln2_b, accumulate, s));
+  }
+  // attention output projection
+  g = lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
+  g.out = b.dO; g.ldc = C;
+  RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
+  RUN("out_wgrad", launch_gemm(lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate), ty, b.split, s));
+  if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
+  // attention
+  RUN("attn_delta", launch_attn_delta(ty, B, T, d.H, d.D, sv.o, b.dO, b.delta, s));
+  RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, s));
+  RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, s));
+  if (cfg->rope || cfg->qk_norm)
+    RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, b.cs, sv.qkv, sv.qkr, b.dqkv, s));
+  // fused QKV projection
+  g = lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
+  g.out = b.da; g.ldc = C;
+  RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
+  RUN("qkv_wgrad", launch_gemm(lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate), ty, b.split, s));
+  if (cfg->bias) RUN("qkv_bias", launch_colsum(ty, N, 3 * C, 3 * C, b.dqkv, gr->b_qkv, accumulate, b.colsum, s));
+  // norm 1 backward + residual
+  RUN("norm1_bwd", launch_norm_bwd(ty, kind, N, C, x, w->ln1_w, b.da, b.dx1, cfg->norm_eps, dx, b.colpart, ln, s));
+  if (ln) {
+    RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln1_w, accumulate, s));
+    if (cfg->bias) RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln1_b, accumulate, s));
+  }
+  return GPT_OK;
+}
+
+int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void* W, const int32_t* targets,
+                         float loss_scale, float* loss, float* nats, void* dh, float* dW, int accumulate, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_cfg(cfg, d);
+  if (st) return st;
+  if (N <= 0) return fail(GPT_ERR_INVALID, "N must be positive");
+  if (!h || !W || !targets || !loss) return fail(GPT_ERR_INVALID, "h, W, targets or loss is NULL");
+  if (!aligned16(h) || !aligned16(W) || !aligned16(dh) || !aligned16(dW) || !aligned16(ws))
+    return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
+  d.B = 1; d.T = N; d.N = N;
+  const size_t need = xent_ws_bytes(d, N);
+  if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Arena wa(ws);
+  XentWs x = xent_layout(d, N, wa);
+  const int C = d.C, V = d.V, ty = d.dtype;
+  float* nt = nats ? nats : x.nats;
+  const bool mfma = ty == 1;
+  // a target outside [0, V) matches no column and leaves NaN in its nats
+  RUN("xent_fill", launch_fill_f32(x.ztgt, N, __builtin_nanf(""), s));
+  for (int c = 0; c < x.nchunk; ++c) {
+    const int v0 = c * x.Vc;
+    const int Vw = std::min(x.Vc, V - v0);
+    const void* Wc = static_cast<const char*>(W) + (size_t)v0 * C * d.es;
+    GemmDesc g = gemm0();
+    g.A = h; g.lda = C; g.B = Wc; g.ldb = C; g.M = N; g.N = Vw; g.K = C;
+    if (mfma) {
+      g.epi = EPI_XENT_STATS;
+      g.tgt = targets; g.col_offset = v0; g.part = x.part; g.part_ld = x.P;
+      int off = 0;
+      for (int q = 0; q < c; ++q) off += 2 * cdiv(std::min(x.Vc, V - q * x.Vc), 256);
+      g.part_off = off; g.ztgt = x.ztgt;
+      RUN("xent_stats_gemm", launch_gemm(g, ty, nullptr, s));
+    } else {
+      g.epi = EPI_F32; g.out = x.zbuf; g.ldc = x.ldz;
+      RUN("xent_logits_gemm", launch_gemm(g, ty, nullptr, s));
+      RUN("xent_rows_stats", launch_xent_rows_stats(N, Vw, v0, x.zbuf, x.ldz, targets, x.run, x.ztgt, c == 0, s));
+    }
+  }
+  RUN("xent_finish", launch_xent_finish(N, mfma ? x.P : 1, mfma ? x.part : x.run, x.ztgt, x.lse, nt, x.loss_part, s));
+  RUN("loss_sum", launch_loss_sum(xent_finish_blocks(N), x.loss_part, loss_scale, loss, s));
+  if (!dh && !dW) return GPT_OK;
+  for (int c = 0; c < x.nchunk; ++c) {
+    const int v0 = c * x.Vc;
+    const int Vw = std::min(x.Vc, V - v0);
+    const void* Wc = static_cast<const char*>(W) + (size_t)v0 * C * d.es;
+    GemmDesc g = gemm0();
+    g.A = h; g.lda = C; g.B = Wc; g.ldb = C; g.M = N; g.N = Vw; g.K = C;
+    if (mfma) {
+      g.epi = EPI_XENT_GRAD; g.out = x.dz; g.ldc = x.ldz;
+      g.tgt = targets; g.col_offset = v0; g.lse = x.lse; g.scale = loss_scale;
+      RUN("xent_grad_gemm", launch_gemm(g, ty, nullptr, s));
+    } else {
+      g.epi = EPI_F32; g.out = x.zbuf; g.ldc = x.ldz;
+      RUN("xent_logits_gemm", launch_gemm(g, ty, nullptr, s));
+      RUN("xent_rows_grad", launch_xent_rows_grad(ty, N, Vw, v0, x.zbuf, x.ldz, targets, x.lse, loss_scale, x.dz, x.ldz, s));
+    }
+    if (dh) {
+      GemmDesc q = gemm0();
+      q.A = x.dz; q.lda = x.ldz; q.a_kmaj = false;
+      q.B = Wc; q.ldb = C; q.b_kmaj = true;
+      q.M = N; q.N = C; q.K = Vw; q.epi = EPI_F32; q.out = x.dh_acc; q.ldc = C; q.accumulate = c > 0;
+      RUN("xent_dh_gemm", launch_gemm(q, ty, x.split, s));
+    }
+    if (dW) {
+      GemmDesc q = gemm0();
+      q.A = x.dz; q.lda = x.ldz; q.a_kmaj = true;
+      q.B = h; q.ldb = C; q.b_kmaj = true;
+      q.M = Vw; q.N = C; q.K = N; q.epi = EPI_F32; q.out = dW + (size_t)v0 * C; q.ldc = C;
+      q.accumulate = accumulate;
+      RUN("xent_dw_gemm", launch_gemm(q, ty, x.split, s));
+    }
+  }
+  if (dh) RUN("xent_dh_convert", launch_f32_to(ty, (long)N * C, x.dh_acc, dh, s));
+  return GPT_OK;
+}
+
+int val_bpb_reduce(int N, const float* nats, const int32_t* targets, const int32_t* token_bytes, int V,
+                   double* sum_nats, int64_t* sum_bytes, void* stream) {
+  if (N <= 0 || V <= 0) return fail(GPT_ERR_INVALID, "N and V must be positive");
+  if (!nats || !targets || !token_bytes || !sum_nats || !sum_bytes)
+    return fail(GPT_ERR_INVALID, "a pointer argument is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("bpb", launch_bpb(N, V, nats, targets, token_bytes, sum_nats, sum_bytes, s));
+  return GPT_OK;
+}
+
+int gpt_embed_fwd(const gpt_config* cfg, int B, int T, const int32_t* ids, const void* wte, const void* wpe,
+                  void* x0, void* stream) {
+  Dims d;
+  int st = check_bt(cfg, B, T, d);
+  if (st) return st;
+  if (!ids || !wte || !x0) return fail(GPT_ERR_INVALID, "ids, wte or x0 is NULL");
+  if (!cfg->rope && !wpe) return fail(GPT_ERR_INVALID, "wpe is NULL with learned positions");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("embed_fwd", launch_embed_fwd(d.dtype, B, T, d.C, d.V, ids, wte, cfg->rope ? nullptr : wpe, x0, s));
+  return GPT_OK;
+}
+
+int gpt_embed_bwd(const gpt_config* cfg, int B, int T, const int32_t* ids, const void* dx0, float* dwte, float* dwpe,
+                  int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_bt(cfg, B, T, d);
+  if (st) return st;
+  if (!ids || !dx0 || !dwte) return fail(GPT_ERR_INVALID, "ids, dx0 or dwte is NULL");
+  const size_t need = embed_ws_bytes(d);
+  if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("embed_bwd", launch_embed_bwd(d.dtype, B, T, d.C, d.V, cfg->block_size, ids, dx0, dwte, dwpe, accumulate, ws,
+                                    ws_bytes, s));
+  return GPT_OK;
+}
+
+int gpt_norm_fwd(const gpt_config* cfg, int N, const void* x, const void* w, const void* b, void* y, float* stats,
+                 void* stream) {
+  Dims d;
+  int st = check_cfg(cfg, d);
+  if (st) return st;
+  if (N <= 0 || !x || !y) return fail(GPT_ERR_INVALID, "N <= 0 or x/y NULL");
+  if (cfg->norm == GPT_NORM_LAYERNORM && !w) return fail(GPT_ERR_INVALID, "LayerNorm gain is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("normf_fwd", launch_norm_fwd(d.dtype, cfg->norm, N, d.C, x, w, opt(cfg, b), cfg->norm_eps, y, stats, s));
+  return GPT_OK;
+}
+
+int gpt_norm_bwd(const gpt_config* cfg, int N, const void* x, const void* w, const void* dy, const void* resid,
+                 void* dx, float* dw, float* db, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  int st = check_cfg(cfg, d);
+  if (st) return st;
+  if (N <= 0 || !x || !dy || !dx) return fail(GPT_ERR_INVALID, "N <= 0 or x/dy/dx NULL");
+  const bool ln = cfg->norm == GPT_NORM_LAYERNORM;
+  if (ln && (!w || !dw)) return fail(GPT_ERR_INVALID, "LayerNorm gain or its gradient is NULL");
+  d.N = N;
+  const size_t need = norm_ws_bytes(d);
+  if (ln && (!ws || ws_bytes < need)) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* colpart = static_cast<float*>(ws);
+  const int nblk = norm_bwd_blocks(N);
+  RUN("normf_bwd", launch_norm_bwd(d.dtype, cfg->norm, N, d.C, x, w, dy, resid, cfg->norm_eps, dx, colpart, ln, s));
+  if (ln) {
+    RUN("normf_cols", launch_colsum_finish(d.C, nblk, colpart, dw, accumulate, s));
+    if (cfg->bias && db) RUN("normf_cols", launch_colsum_finish(d.C, nblk, colpart + (size_t)nblk * d.C, db, accumulate, s));
+  }
+  return GPT_OK;
+}
+
+}  // extern "C"

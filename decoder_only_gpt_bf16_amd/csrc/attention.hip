@@ -1,0 +1,856 @@
+// Causal self-attention forward/backward, RoPE + QK-norm, and the
+// backward's row-dot preprocessing.
+//
+// Math ("nanoGPT — Karpathy's minimal GPT pretraining repo", model.py,
+// CausalSelfAttention: per head S = q k^T / sqrt(D), future positions
+// masked, P = softmax(S), O = P v; the nanochat-d20 form applies RoPE and a
+// parameter-free RMS QK-norm to q and k first).
+//
+// bf16 MFMA kernels (head_dim 64 or 128), wave64, v_mfma_f32_32x32x16_bf16:
+//  * forward: a workgroup owns 128 queries of one (batch, head), one wave per
+//    32 queries; K and V tiles of 64 keys are staged in LDS (double buffer).
+//    Each wave computes S^T = K Q^T so that a lane owns one query and its
+//    softmax statistics stay in the lane (one cross-half exchange per
+//    reduction); P^T is fed straight from the accumulators as the B operand
+//    of O^T = V^T P^T.  Online softmax in the log2 domain; fully masked
+//    tiles are skipped per wave, the causal mask is applied only to tiles
+//    that cross the diagonal; log-sum-exp is saved for the backward.
+//  * backward: two passes, no floating-point atomics (bitwise
+//    deterministic).  dK/dV: a workgroup owns 128 keys, loops over query
+//    tiles, recomputes P from the saved log-sum-exp, accumulates
+//    dV^T = dO^T P and dK^T = Q^T dS.  dQ: a workgroup owns 128 queries,
+//    loops over key tiles, accumulates dQ^T = K^T dS^T.
+//  * MFMA k-slot order: within a 16-wide reduction step, lane half h and
+//    slot e of both operands stand for the same reduction index
+//    16 ks + 4 h + e (slots 0..3) or 16 ks + 8 + 4 h + e (slots 4..7), which
+//    is where a 32x32 accumulator keeps its rows; operands read from LDS
+//    use the same mapping.
+// SIMT kernels cover fp32 storage and other head dims (any D <= 128).
+#include "kernels.h"
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8 u4_bf8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 u22_bf8(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+// element e (0..7) of a 16-byte vector of bf16, as raw 16 bits
+__device__ __forceinline__ uint32_t elem16(const uint4& v, int e) {
+  const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Pack accumulator registers 4g0..4g0+3 and 4g0+4..4g0+7 of a 32x32 tile as
+// the 8 bf16 k-slots of a B operand.
+__device__ __forceinline__ bf16x8 pack_slots(const float* p, int g0) {
+  uint4 u;
+  u.x = pack2(p[4 * g0 + 0], p[4 * g0 + 1]);
+  u.y = pack2(p[4 * g0 + 2], p[4 * g0 + 3]);
+  u.z = pack2(p[4 * g0 + 4], p[4 * g0 + 5]);
+  u.w = pack2(p[4 * g0 + 6], p[4 * g0 + 7]);
+  return u4_bf8(u);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile staging.  "Row" tiles: ROWS x D bf16, 16-byte unit c of row r at
+// c ^ (r & 7).  "Transposed" tiles: D x ROWS, 8-byte units of 4 rows, unit u
+// of line d at u ^ ((d >> 1) & 15); ROWS = 64 gives 16 units per line.
+// ---------------------------------------------------------------------------
+template <int D>
+struct RowTile {
+  static constexpr int KU = D / 8;
+  static constexpr int UNITS = 64 * KU;
+  static constexpr int PER = UNITS / 256;
+  uint4 v[PER];
+  // src row r is at base + r * ld; rows >= nvalid are zero
+  __device__ __forceinline__ void load(const bf16* base, long ld, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      const int r = u / KU, c = u % KU;
+      v[i] = (r < nvalid) ? ld16(base + (long)r * ld + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(uint4* s) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      const int r = u / KU, c = u % KU;
+      s[r * KU + (c ^ (r & 7))] = v[i];
+    }
+  }
+};
+
+template <int D>
+struct TrTile {
+  static constexpr int NSUB = 8 * (D / 8);  // 8 row-groups x D/8 column groups
+  uint4 v[8];
+  // thread t < NSUB: row group kg = t & 7 (rows 8kg..8kg+7), col group dg = t >> 3
+  __device__ __forceinline__ void load(const bf16* base, long ld, int nvalid) {
+    const int t = threadIdx.x;
+    if (t >= NSUB) return;
+    const int kg = t & 7, dg = t >> 3;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 8 * kg + j;
+      v[j] = (r < nvalid) ? ld16(base + (long)r * ld + 8 * dg) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(uint2* s) const {
+    const int t = threadIdx.x;
+    if (t >= NSUB) return;
+    const int kg = t & 7, dg = t >> 3;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * dg + e;
+      const int sw = (d >> 1) & 15;
+      uint2 a, b;
+      a.x = elem16(v[0], e) | (elem16(v[1], e) << 16);
+      a.y = elem16(v[2], e) | (elem16(v[3], e) << 16);
+      b.x = elem16(v[4], e) | (elem16(v[5], e) << 16);
+      b.y = elem16(v[6], e) | (elem16(v[7], e) << 16);
+      s[d * 16 + ((2 * kg) ^ sw)] = a;
+      s[d * 16 + ((2 * kg + 1) ^ sw)] = b;
+    }
+  }
+};
+
+// A-operand fragment from a row tile: row r, k-step s (16 wide), lane half h.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const uint4* s, int r, int ks, int hf) {
+  constexpr int KU = D / 8;
+  return u4_bf8(s[r * KU + ((2 * ks + hf) ^ (r & 7))]);
+}
+// A-operand fragment from a transposed tile: line d, reduction step ks over 16 rows.
+__device__ __forceinline__ bf16x8 tr_frag(const uint2* s, int d, int ks, int hf) {
+  const int sw = (d >> 1) & 15;
+  return u22_bf8(s[d * 16 + ((4 * ks + hf) ^ sw)], s[d * 16 + ((4 * ks + 2 + hf) ^ sw)]);
+}
+
+// ------------------------------------------------------------ forward (MFMA)
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16* __restrict__ qkv,
+                                                        bf16* __restrict__ o, float* __restrict__ lse,
+                                                        float scale_log2) {
+  constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
+  __shared__ uint4 sK[2][64 * KU];
+  __shared__ uint2 sV[2][D * 16];
+  const int nqb = (T + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const bf16* Qg = qkv + (long)b * T * ld + h * D;
+  const bf16* Kg = Qg + C;
+  const bf16* Vg = Qg + 2 * C;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hf = lane >> 5;
+  const int q0 = qb * 128;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + li;
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = u4_bf8(qi < T ? ld16(Qg + (long)qi * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int kv_end = min(T, q0 + 128);
+  const int ntiles = (kv_end + 63) / 64;
+  RowTile<D> stK;
+  TrTile<D> stV;
+  stK.load(Kg, ld, T);
+  stV.load(Vg, ld, T);
+  stK.store(sK[0]);
+  stV.store(sV[0]);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < ntiles;
+    const int kv0 = t * 64;
+    if (more) {
+      stK.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+      stV.load(Vg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+    }
+    if (kv0 <= qw + 31 && qw < T) {
+      f32x16 st[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[jt][r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sK[cur], 32 * jt + li, s, hf), qf[s],
+                                                           st[jt], 0, 0, 0);
+      }
+      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
+      float p[2][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = st[jt][r] * scale_log2;
+          if (need_mask) {
+            const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (j > qi || j >= T) x = -INFINITY;
+          }
+          p[jt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const bool dead = (m_new == -INFINITY);
+      const float corr = dead ? 1.0f : exp2f(m_run - m_new);
+      float rs = 0.0f;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = dead ? 0.0f : exp2f(p[jt][r] - m_new);
+          p[jt][r] = e;
+          rs += e;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l_run = l_run * corr + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pb = pack_slots(p[ks >> 1], 2 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sV[cur], 32 * dt + li, ks, hf), pb, acc[dt],
+                                                            0, 0, 0);
+      }
+    }
+    if (more) {
+      stK.store(sK[cur ^ 1]);
+      stV.store(sV[cur ^ 1]);
+    }
+    __syncthreads();
+  }
+
+  if (qi < T) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    bf16* orow = o + ((long)b * T + qi) * C + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hf;
+        uint2 u;
+        u.x = pack2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
+        u.y = pack2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+    if (hf == 0) lse[((long)b * H + h) * T + qi] = (m_run + log2f(l_run)) * LN2;
+  }
+}
+
+// ------------------------------------------------------ backward dK, dV (MFMA)
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
+                                                             const bf16* __restrict__ dO,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ delta,
+                                                             bf16* __restrict__ dqkv, float scale_log2,
+                                                             float scale) {
+  constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
+  __shared__ uint4 sQ[2][64 * KU];
+  __shared__ uint4 sdO[2][64 * KU];
+  __shared__ uint2 sQt[2][D * 16];
+  __shared__ uint2 sdOt[2][D * 16];
+  __shared__ float sL[2][64], sDl[2][64];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const bf16* Qg = qkv + (long)b * T * ld + h * D;
+  const bf16* Kg = Qg + C;
+  const bf16* Vg = Qg + 2 * C;
+  const bf16* dOg = dO + (long)b * T * C + h * D;
+  const float* Lg = lse + ((long)b * H + h) * T;
+  const float* Dg = delta + ((long)b * H + h) * T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hf = lane >> 5;
+  const int k0 = blockIdx.x * 128;
+  const int kw = k0 + 32 * wave;
+  const int kj = kw + li;
+
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = u4_bf8(kj < T ? ld16(Kg + (long)kj * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+    vf[s] = u4_bf8(kj < T ? ld16(Vg + (long)kj * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[dt][r] = 0.0f; dv[dt][r] = 0.0f; }
+
+  const int t_begin = k0 / 64;
+  const int t_end = (T + 63) / 64;
+  RowTile<D> stQ, stdO;
+  TrTile<D> stQt, stdOt;
+  auto stage_load = [&](int t) {
+    const int qt0 = t * 64;
+    stQ.load(Qg + (long)qt0 * ld, ld, T - qt0);
+    stdO.load(dOg + (long)qt0 * C, C, T - qt0);
+    stQt.load(Qg + (long)qt0 * ld, ld, T - qt0);
+    stdOt.load(dOg + (long)qt0 * C, C, T - qt0);
+  };
+  auto stage_store = [&](int t, int buf) {
+    stQ.store(sQ[buf]);
+    stdO.store(sdO[buf]);
+    stQt.store(sQt[buf]);
+    stdOt.store(sdOt[buf]);
+    const int qt0 = t * 64;
+    if (threadIdx.x < 64) {
+      const int q = qt0 + threadIdx.x;
+      sL[buf][threadIdx.x] = q < T ? Lg[q] * LOG2E : 0.0f;
+      sDl[buf][threadIdx.x] = q < T ? Dg[q] : 0.0f;
+    }
+  };
+  if (t_begin < t_end) {
+    stage_load(t_begin);
+    stage_store(t_begin, 0);
+  }
+  __syncthreads();
+  for (int t = t_begin; t < t_end; ++t) {
+    const int cur = (t - t_begin) & 1;
+    const bool more = t + 1 < t_end;
+    const int qt0 = t * 64;
+    if (more) stage_load(t + 1);
+    if (qt0 + 63 >= kw && kw < T) {
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { S[it][r] = 0.0f; dP[it][r] = 0.0f; }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          S[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sQ[cur], 32 * it + li, s, hf), kf[s], S[it],
+                                                          0, 0, 0);
+          dP[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sdO[cur], 32 * it + li, s, hf), vf[s],
+                                                           dP[it], 0, 0, 0);
+        }
+      }
+      float p[2][16], ds[2][16];
+      const bool need_mask = (qt0 < kw + 31) || (qt0 + 64 > T) || (kw + 32 > T);
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int il = 32 * it + 8 * g + 4 * hf;
+          const float4 L4 = *reinterpret_cast<const float4*>(&sL[cur][il]);
+          const float4 D4 = *reinterpret_cast<const float4*>(&sDl[cur][il]);
+          const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
+          const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float pv = exp2f(fmaf(S[it][r], scale_log2, -Ls[e]));
+            if (need_mask) {
+              const int qi = qt0 + il + e;
+              if (qi < kj || qi >= T || kj >= T) pv = 0.0f;
+            }
+            p[it][r] = pv;
+            ds[it][r] = pv * (dP[it][r] - Ds[e]);
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pb = pack_slots(p[ks >> 1], 2 * (ks & 1));
+        const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sdOt[cur], 32 * dt + li, ks, hf), pb, dv[dt], 0,
+                                                           0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sQt[cur], 32 * dt + li, ks, hf), db, dk[dt], 0,
+                                                           0, 0);
+        }
+      }
+    }
+    if (more) stage_store(t + 1, cur ^ 1);
+    __syncthreads();
+  }
+  if (kj < T) {
+    bf16* krow = dqkv + ((long)b * T + kj) * ld + C + h * D;
+    bf16* vrow = krow + C;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hf;
+        uint2 u;
+        u.x = pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale);
+        u.y = pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale);
+        *reinterpret_cast<uint2*>(krow + d) = u;
+        u.x = pack2(dv[dt][4 * g], dv[dt][4 * g + 1]);
+        u.y = pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
+        *reinterpret_cast<uint2*>(vrow + d) = u;
+      }
+  }
+}
+
+// ---------------------------------------------------------- backward dQ (MFMA)
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
+                                                           const bf16* __restrict__ dO,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta,
+                                                           bf16* __restrict__ dqkv, float scale_log2,
+                                                           float scale) {
+  constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
+  __shared__ uint4 sK[2][64 * KU];
+  __shared__ uint4 sV[2][64 * KU];
+  __shared__ uint2 sKt[2][D * 16];
+  const int nqb = (T + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const bf16* Qg = qkv + (long)b * T * ld + h * D;
+  const bf16* Kg = Qg + C;
+  const bf16* Vg = Qg + 2 * C;
+  const bf16* dOg = dO + (long)b * T * C + h * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, hf = lane >> 5;
+  const int q0 = qb * 128;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + li;
+
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = u4_bf8(qi < T ? ld16(Qg + (long)qi * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+    df[s] = u4_bf8(qi < T ? ld16(dOg + (long)qi * C + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+  }
+  const long row_lse = ((long)b * H + h) * T + qi;
+  const float L2 = qi < T ? lse[row_lse] * LOG2E : 0.0f;
+  const float Dl = qi < T ? delta[row_lse] : 0.0f;
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.0f;
+
+  const int kv_end = min(T, q0 + 128);
+  const int ntiles = (kv_end + 63) / 64;
+  RowTile<D> stK, stV;
+  TrTile<D> stKt;
+  stK.load(Kg, ld, T);
+  stV.load(Vg, ld, T);
+  stKt.load(Kg, ld, T);
+  stK.store(sK[0]);
+  stV.store(sV[0]);
+  stKt.store(sKt[0]);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < ntiles;
+    const int kv0 = t * 64;
+    if (more) {
+      stK.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+      stV.load(Vg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+      stKt.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+    }
+    if (kv0 <= qw + 31 && qw < T) {
+      f32x16 St[2], dPt[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { St[jt][r] = 0.0f; dPt[jt][r] = 0.0f; }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          St[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sK[cur], 32 * jt + li, s, hf), qf[s], St[jt],
+                                                           0, 0, 0);
+          dPt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sV[cur], 32 * jt + li, s, hf), df[s],
+                                                            dPt[jt], 0, 0, 0);
+        }
+      }
+      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T) || (qw + 32 > T);
+      float ds[2][16];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = exp2f(fmaf(St[jt][r], scale_log2, -L2));
+          if (need_mask) {
+            const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (j > qi || j >= T || qi >= T) pv = 0.0f;
+          }
+          ds[jt][r] = pv * (dPt[jt][r] - Dl);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sKt[cur], 32 * dt + li, ks, hf), db, dq[dt], 0, 0,
+                                                           0);
+      }
+    }
+    if (more) {
+      stK.store(sK[cur ^ 1]);
+      stV.store(sV[cur ^ 1]);
+      stKt.store(sKt[cur ^ 1]);
+    }
+    __syncthreads();
+  }
+  if (qi < T) {
+    bf16* qrow = dqkv + ((long)b * T + qi) * ld + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hf;
+        uint2 u;
+        u.x = pack2(dq[dt][4 * g] * scale, dq[dt][4 * g + 1] * scale);
+        u.y = pack2(dq[dt][4 * g + 2] * scale, dq[dt][4 * g + 3] * scale);
+        *reinterpret_cast<uint2*>(qrow + d) = u;
+      }
+  }
+}
+
+// ------------------------------------------------------------ SIMT fallbacks
+// One thread per query (forward, dQ) or per key (dK, dV); fp32 arithmetic.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_fwd_simt(int TT, int H, const T* __restrict__ qkv, T* __restrict__ o,
+                                                    float* __restrict__ lse, float scale) {
+  const int qi = blockIdx.x * 64 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (qi >= TT) return;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const T* base = qkv + (long)b * TT * ld + h * D;
+  float q[D], acc[D];
+  for (int d = 0; d < D; ++d) { q[d] = to_f32(base[(long)qi * ld + d]) * scale; acc[d] = 0.0f; }
+  float m = -INFINITY, l = 0.0f;
+  for (int j = 0; j <= qi; ++j) {
+    const T* kr = base + (long)j * ld + C;
+    float s = 0.0f;
+    for (int d = 0; d < D; ++d) s = fmaf(q[d], to_f32(kr[d]), s);
+    const float mn = fmaxf(m, s);
+    const float corr = expf(m - mn);
+    const float pj = expf(s - mn);
+    l = l * corr + pj;
+    const T* vr = kr + C;
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(pj, to_f32(vr[d]), acc[d] * corr);
+    m = mn;
+  }
+  T* orow = o + ((long)b * TT + qi) * C + h * D;
+  for (int d = 0; d < D; ++d) orow[d] = from_f32<T>(acc[d] / l);
+  lse[((long)b * H + h) * TT + qi] = m + logf(l);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_bwd_dq_simt(int TT, int H, const T* __restrict__ qkv,
+                                                       const T* __restrict__ dO, const float* __restrict__ lse,
+                                                       const float* __restrict__ delta, T* __restrict__ dqkv,
+                                                       float scale) {
+  const int qi = blockIdx.x * 64 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (qi >= TT) return;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const T* base = qkv + (long)b * TT * ld + h * D;
+  const T* dob = dO + ((long)b * TT + qi) * C + h * D;
+  float q[D], g[D], acc[D];
+  for (int d = 0; d < D; ++d) { q[d] = to_f32(base[(long)qi * ld + d]); g[d] = to_f32(dob[d]); acc[d] = 0.0f; }
+  const long rl = ((long)b * H + h) * TT + qi;
+  const float L = lse[rl], Dl = delta[rl];
+  for (int j = 0; j <= qi; ++j) {
+    const T* kr = base + (long)j * ld + C;
+    const T* vr = kr + C;
+    float s = 0.0f, dp = 0.0f;
+    for (int d = 0; d < D; ++d) { s = fmaf(q[d], to_f32(kr[d]), s); dp = fmaf(g[d], to_f32(vr[d]), dp); }
+    const float p = expf(s * scale - L);
+    const float ds = p * (dp - Dl);
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, to_f32(kr[d]), acc[d]);
+  }
+  T* out = dqkv + ((long)b * TT + qi) * ld + h * D;
+  for (int d = 0; d < D; ++d) out[d] = from_f32<T>(acc[d] * scale);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_simt(int TT, int H, const T* __restrict__ qkv,
+                                                         const T* __restrict__ dO, const float* __restrict__ lse,
+                                                         const float* __restrict__ delta, T* __restrict__ dqkv,
+                                                         float scale) {
+  const int kj = blockIdx.x * 64 + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (kj >= TT) return;
+  const int C = H * D;
+  const long ld = 3L * C;
+  const T* base = qkv + (long)b * TT * ld + h * D;
+  float k[D], v[D], dk[D], dv[D];
+  for (int d = 0; d < D; ++d) {
+    k[d] = to_f32(base[(long)kj * ld + C + d]);
+    v[d] = to_f32(base[(long)kj * ld + 2 * C + d]);
+    dk[d] = 0.0f; dv[d] = 0.0f;
+  }
+  for (int i = kj; i < TT; ++i) {
+    const T* qr = base + (long)i * ld;
+    const T* gr = dO + ((long)b * TT + i) * C + h * D;
+    const long rl = ((long)b * H + h) * TT + i;
+    float s = 0.0f, dp = 0.0f;
+    for (int d = 0; d < D; ++d) { s = fmaf(to_f32(qr[d]), k[d], s); dp = fmaf(to_f32(gr[d]), v[d], dp); }
+    const float p = expf(s * scale - lse[rl]);
+    const float ds = p * (dp - delta[rl]);
+    for (int d = 0; d < D; ++d) { dk[d] = fmaf(ds, to_f32(qr[d]), dk[d]); dv[d] = fmaf(p, to_f32(gr[d]), dv[d]); }
+  }
+  T* out = dqkv + ((long)b * TT + kj) * ld + C + h * D;
+  for (int d = 0; d < D; ++d) { out[d] = from_f32<T>(dk[d] * scale); out[C + d] = from_f32<T>(dv[d]); }
+}
+
+// ----------------------------------------------------- RoPE / QK-norm, delta
+__global__ void rope_table_k(int T, int D, double base, float2* cs) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = D / 2;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx % half;
+  const double theta = pow(base, -2.0 * i / D);
+  double sn, c;
+  sincos((double)t * theta, &sn, &c);
+  cs[idx] = make_float2((float)c, (float)sn);
+}
+
+// One wavefront per (row, head, q|k); lane i < D/2 handles pair (i, i + D/2).
+template <typename T>
+__global__ __launch_bounds__(256) void qk_fwd_k(int N, int TT, int H, int D, int rope, int qk_norm, float eps,
+                                                const float2* __restrict__ cs, T* __restrict__ qkv,
+                                                float* __restrict__ rstd) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= 2L * N * H) return;
+  const int which = (int)(w / ((long)N * H));
+  const long rem = w % ((long)N * H);
+  const int n = (int)(rem / H), h = (int)(rem % H);
+  const int C = H * D, half = D / 2;
+  const int t = n % TT;
+  T* v = qkv + (long)n * 3 * C + which * C + h * D;
+  // D <= 128: one pass of 64 lanes covers every pair
+  const int i = lane;
+  float a = 0.0f, bb = 0.0f;
+  if (i < half) { a = to_f32(v[i]); bb = to_f32(v[i + half]); }
+  float r = 1.0f;
+  if (qk_norm) {
+    const float ss = wave_sum(a * a + bb * bb);
+    r = 1.0f / sqrtf(ss / D + eps);
+  }
+  if (i < half) {
+    float na = a, nb = bb;
+    if (rope) {
+      const float2 c = cs[t * half + i];
+      na = a * c.x - bb * c.y;
+      nb = a * c.y + bb * c.x;
+    }
+    v[i] = from_f32<T>(na * r);
+    v[i + half] = from_f32<T>(nb * r);
+  }
+  if (qk_norm && lane == 0) rstd[(long)which * N * H + (long)n * H + h] = r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void qk_bwd_k(int N, int TT, int H, int D, int rope, int qk_norm,
+                                                const float2* __restrict__ cs, const T* __restrict__ qkv,
+                                                const float* __restrict__ rstd, T* __restrict__ dqkv) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= 2L * N * H) return;
+  const int which = (int)(w / ((long)N * H));
+  const long rem = w % ((long)N * H);
+  const int n = (int)(rem / H), h = (int)(rem % H);
+  const int C = H * D, half = D / 2;
+  const int t = n % TT;
+  const long off = (long)n * 3 * C + which * C + h * D;
+  const int i = lane;
+  float ga = 0.0f, gb = 0.0f, ya = 0.0f, yb = 0.0f;
+  if (i < half) {
+    ga = to_f32(dqkv[off + i]); gb = to_f32(dqkv[off + i + half]);
+    ya = to_f32(qkv[off + i]); yb = to_f32(qkv[off + i + half]);
+  }
+  if (qk_norm) {
+    const float r = rstd[(long)which * N * H + (long)n * H + h];
+    const float m = wave_sum(ga * ya + gb * yb) / D;
+    ga = r * (ga - ya * m);
+    gb = r * (gb - yb * m);
+  }
+  if (i < half) {
+    if (rope) {
+      const float2 c = cs[t * half + i];
+      const float na = ga * c.x + gb * c.y;
+      const float nb = -ga * c.y + gb * c.x;
+      ga = na; gb = nb;
+    }
+    dqkv[off + i] = from_f32<T>(ga);
+    dqkv[off + i + half] = from_f32<T>(gb);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void delta_k(int N, int TT, int H, int D, const T* __restrict__ o,
+                                               const T* __restrict__ dO, float* __restrict__ delta) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)N * H) return;
+  const int n = (int)(idx / H), h = (int)(idx % H);
+  const int C = H * D;
+  const T* a = o + (long)n * C + h * D;
+  const T* g = dO + (long)n * C + h * D;
+  float s = 0.0f;
+  for (int d = 0; d < D; d += 8) {
+    float x[8], y[8];
+    Vec8<T>::load(a + d, x);
+    Vec8<T>::load(g + d, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(x[e], y[e], s);
+  }
+  const int b = n / TT, t = n % TT;
+  delta[((long)b * H + h) * TT + t] = s;
+}
+
+template <typename T, int D>
+hipError_t simt_all(int which, int B, int TT, int H, const void* qkv, const void* dO, void* out, float* lse,
+                    const float* delta, hipStream_t s) {
+  const float scale = 1.0f / sqrtf((float)D);
+  dim3 grid(cdiv(TT, 64), H, B);
+  if (which == 0)
+    hipLaunchKernelGGL((attn_fwd_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (T*)out, lse, scale);
+  else if (which == 1)
+    hipLaunchKernelGGL((attn_bwd_dq_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (const T*)dO, lse,
+                       delta, (T*)out, scale);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (const T*)dO, lse,
+                       delta, (T*)out, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t simt_dispatch(int which, int B, int TT, int H, int D, const void* qkv, const void* dO, void* out,
+                         float* lse, const float* delta, hipStream_t s) {
+  switch (D) {
+    case 16: return simt_all<T, 16>(which, B, TT, H, qkv, dO, out, lse, delta, s);
+    case 32: return simt_all<T, 32>(which, B, TT, H, qkv, dO, out, lse, delta, s);
+    case 64: return simt_all<T, 64>(which, B, TT, H, qkv, dO, out, lse, delta, s);
+    case 128: return simt_all<T, 128>(which, B, TT, H, qkv, dO, out, lse, delta, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool attn_mfma_supported(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
+
+hipError_t launch_rope_table(int T, int D, float base, float2* cs, hipStream_t s) {
+  const int n = T * (D / 2);
+  hipLaunchKernelGGL(rope_table_k, dim3(cdiv(n, 256)), dim3(256), 0, s, T, D, (double)base, cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_fwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm, float eps,
+                         const float2* cs, void* qkv, float* rstd, hipStream_t s) {
+  const int N = B * T;
+  const long waves = 2L * N * H;
+  dim3 grid((unsigned)cdiv(waves, 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(qk_fwd_k<bf16>, grid, dim3(256), 0, s, N, T, H, D, rope, qk_norm, eps, cs, (bf16*)qkv, rstd);
+  else
+    hipLaunchKernelGGL(qk_fwd_k<float>, grid, dim3(256), 0, s, N, T, H, D, rope, qk_norm, eps, cs, (float*)qkv, rstd);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm, const float2* cs,
+                         const void* qkv, const float* rstd, void* dqkv, hipStream_t s) {
+  const int N = B * T;
+  const long waves = 2L * N * H;
+  dim3 grid((unsigned)cdiv(waves, 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(qk_bwd_k<bf16>, grid, dim3(256), 0, s, N, T, H, D, rope, qk_norm, cs, (const bf16*)qkv, rstd,
+                       (bf16*)dqkv);
+  else
+    hipLaunchKernelGGL(qk_bwd_k<float>, grid, dim3(256), 0, s, N, T, H, D, rope, qk_norm, cs, (const float*)qkv,
+                       rstd, (float*)dqkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qkv, void* o, float* lse,
+                           hipStream_t s) {
+  if (attn_mfma_supported(dtype, D)) {
+    const float scale_log2 = LOG2E / sqrtf((float)D);
+    dim3 grid(cdiv(T, 128), H, B);
+    if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, T, H, (const bf16*)qkv, (bf16*)o, lse, scale_log2);
+    else
+      hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, T, H, (const bf16*)qkv, (bf16*)o, lse, scale_log2);
+    return hipGetLastError();
+  }
+  if (dtype == 1) return simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, s);
+  return simt_dispatch<float>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, s);
+}
+
+hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO, float* delta,
+                             hipStream_t s) {
+  const int N = B * T;
+  dim3 grid(cdiv((long)N * H, 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(delta_k<bf16>, grid, dim3(256), 0, s, N, T, H, D, (const bf16*)o, (const bf16*)dO, delta);
+  else
+    hipLaunchKernelGGL(delta_k<float>, grid, dim3(256), 0, s, N, T, H, D, (const float*)o, (const float*)dO, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+                                const float* lse, const float* delta, void* dqkv, hipStream_t s) {
+  if (attn_mfma_supported(dtype, D)) {
+    const float scale = 1.0f / sqrtf((float)D);
+    const float scale_log2 = LOG2E * scale;
+    dim3 g(cdiv(T, 128), H, B);
+    if (D == 128)
+      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+                         delta, (bf16*)dqkv, scale_log2, scale);
+    else
+      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+                         delta, (bf16*)dqkv, scale_log2, scale);
+    return hipGetLastError();
+  }
+  if (dtype == 1) return simt_dispatch<bf16>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+  return simt_dispatch<float>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+}
+
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+                              const float* lse, const float* delta, void* dqkv, hipStream_t s) {
+  if (attn_mfma_supported(dtype, D)) {
+    const float scale = 1.0f / sqrtf((float)D);
+    const float scale_log2 = LOG2E * scale;
+    dim3 g(cdiv(T, 128), H, B);
+    if (D == 128)
+      hipLaunchKernelGGL(attn_bwd_dq_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+                         delta, (bf16*)dqkv, scale_log2, scale);
+    else
+      hipLaunchKernelGGL(attn_bwd_dq_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+                         delta, (bf16*)dqkv, scale_log2, scale);
+    return hipGetLastError();
+  }
+  if (dtype == 1) return simt_dispatch<bf16>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+  return simt_dispatch<float>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+}

@@ -1,0 +1,147 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+#include "common.h"
+
+// ---------------------------------------------------------------------------
+// GEMM: C(m, n) = sum_k A(m, k) * B(n, k), fp32 accumulation.
+//   A row-major [M, lda] with k contiguous        (a_kmaj = false), or
+//             [K, lda] with m contiguous          (a_kmaj = true);
+//   B row-major [N, ldb] with k contiguous        (b_kmaj = false), or
+//             [K, ldb] with n contiguous          (b_kmaj = true).
+// Forward Linear: A = activations, B = weight [out, in] (both k-contiguous).
+// Input gradient dX = dY W: B = W given as [K = out, N = in] (b_kmaj).
+// Weight gradient dW = dY^T X: A = dY as [K = tokens, M = out] (a_kmaj),
+//   B = X as [K = tokens, N = in] (b_kmaj).
+// ---------------------------------------------------------------------------
+enum EpiKind {
+  EPI_STORE = 0,      // out(T) = acc (+ bias[n]) (+ resid[m, n])
+  EPI_GELU = 1,       // u = acc + bias[n]; out(T) = u; out2(T) = gelu(u)
+  EPI_GELU_BWD = 2,   // out(T) = acc * gelu'(aux[m, n])
+  EPI_F32 = 3,        // out(f32) = acc (+ out if accumulate)
+  EPI_XENT_STATS = 4, // per (row, 128-col block): max and sum exp; target logit
+  EPI_XENT_GRAD = 5,  // out(T) = (exp(acc - lse[m]) - [n + col_offset == tgt[m]]) * scale
+};
+
+struct GemmParams {
+  const void* A;
+  const void* B;
+  long lda, ldb;
+  int M, N, K;
+  int k_split;            // K elements handled per blockIdx.z
+  int tiles_m, tiles_n;
+  // epilogue
+  void* out;
+  long ldc;
+  long split_stride;      // elements between per-split partial outputs
+  const void* bias;
+  const void* resid;
+  long ldr;
+  void* out2;
+  const void* aux;
+  long ldaux;
+  int accumulate;
+  // cross-entropy epilogues
+  const int32_t* tgt;
+  int col_offset;
+  float2* part;           // [M, part_ld] (max, sum exp) partials
+  int part_ld;
+  int part_off;
+  float* ztgt;            // [M] target logits
+  const float* lse;       // [M]
+  float scale;
+};
+
+struct GemmDesc {
+  const void* A; long lda; bool a_kmaj;
+  const void* B; long ldb; bool b_kmaj;
+  int M, N, K;
+  int epi;
+  void* out; long ldc;
+  const void* bias;
+  const void* resid; long ldr;
+  void* out2;
+  const void* aux; long ldaux;
+  int accumulate;
+  const int32_t* tgt; int col_offset; float2* part; int part_ld; int part_off;
+  float* ztgt; const float* lse; float scale;
+};
+
+// Bytes of split-K scratch launch_gemm may use for this problem (0 if none).
+size_t gemm_split_scratch_bytes(const GemmDesc& d, int dtype);
+// Columns per cross-entropy partial of the bf16 MFMA path.
+int xent_part_cols();
+// Launch; `ws` provides split-K scratch of gemm_split_scratch_bytes().
+hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Norms, embeddings, attention, cross-entropy, reductions.
+// ---------------------------------------------------------------------------
+hipError_t launch_norm_fwd(int dtype, int kind, int N, int C, const void* x, const void* w,
+                           const void* b, float eps, void* y, float* stats, hipStream_t s);
+// dx = norm_bwd(dy) (+ resid); column partial sums of dy*xhat and dy into
+// colpart [2][nblk][C] (when want_cols), reduced by launch_colsum_finish.
+hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, const void* w,
+                           const void* dy, const void* resid, float eps, void* dx,
+                           float* colpart, int want_cols, hipStream_t s);
+int norm_bwd_blocks(int N);
+hipError_t launch_colsum_finish(int C, int nblk, const float* part, float* out, int accumulate,
+                                hipStream_t s);
+// Column sums of a [N, C] matrix (storage dtype) into out fp32 [C] (bias gradients).
+size_t colsum_scratch_bytes(int N, int C);
+hipError_t launch_colsum(int dtype, int N, int C, long ld, const void* x, float* out,
+                         int accumulate, float* scratch, hipStream_t s);
+
+// ids outside [0, V) give a zero token embedding (no out-of-range read).
+hipError_t launch_embed_fwd(int dtype, int B, int T, int C, int V, const int32_t* ids, const void* wte,
+                            const void* wpe, void* x0, hipStream_t s);
+size_t embed_bwd_scratch_bytes(int N, int V);
+// dwpe [wpe_rows, C] (rows >= T receive 0) or NULL.  ids outside [0, V)
+// contribute nothing.
+hipError_t launch_embed_bwd(int dtype, int B, int T, int C, int V, int wpe_rows, const int32_t* ids,
+                            const void* dx0, float* dwte, float* dwpe, int accumulate, void* scratch,
+                            size_t scratch_bytes, hipStream_t s);
+
+// RoPE angle table: cs[t * (D/2) + i] = (cos, sin)(t * base^(-2i/D)).
+hipError_t launch_rope_table(int T, int D, float base, float2* cs, hipStream_t s);
+// In place on the q and k thirds of qkv [N, 3C]: RoPE then QK-norm; saves
+// 1/rms of q and k per (row, head) into rstd [2][N][H] when qk_norm.
+hipError_t launch_qk_fwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm, float eps,
+                         const float2* cs, void* qkv, float* rstd, hipStream_t s);
+// In place on dq, dk thirds of dqkv: QK-norm backward (needs the normalised
+// q, k from qkv and rstd), then the inverse rotation.
+hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm,
+                         const float2* cs, const void* qkv, const float* rstd, void* dqkv,
+                         hipStream_t s);
+// Causal attention forward: q, k, v inside qkv [N, 3C]; o [N, C]; lse fp32 [B, H, T].
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qkv, void* o,
+                           float* lse, hipStream_t s);
+// delta[b, h, t] = sum_d dO * O (fp32 [B, H, T]).
+hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO,
+                             float* delta, hipStream_t s);
+// Attention backward into the dk | dv thirds and the dq third of dqkv [N, 3C].
+hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+                                const float* lse, const float* delta, void* dqkv, hipStream_t s);
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+                              const float* lse, const float* delta, void* dqkv, hipStream_t s);
+bool attn_mfma_supported(int dtype, int D);
+
+// Cross-entropy reductions.
+// Combine per-row partials into lse, nats = lse - ztgt, block loss partials.
+hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, float* lse,
+                              float* nats, float* loss_part, hipStream_t s);
+hipError_t launch_loss_sum(int nblk, const float* loss_part, float scale, float* loss,
+                           hipStream_t s);
+int xent_finish_blocks(int N);
+// Generic path: running row statistics over a materialised fp32 logit chunk.
+hipError_t launch_xent_rows_stats(int N, int Vc, int v0, const float* z, long ldz,
+                                  const int32_t* tgt, float2* run, float* ztgt, int first,
+                                  hipStream_t s);
+hipError_t launch_xent_rows_grad(int dtype, int N, int Vc, int v0, const float* z, long ldz,
+                                 const int32_t* tgt, const float* lse, float scale, void* dz,
+                                 long lddz, hipStream_t s);
+hipError_t launch_f32_to(int dtype, long n, const float* src, void* dst, hipStream_t s);
+hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t s);
+
+// targets outside [0, V) count as zero-byte tokens.
+hipError_t launch_bpb(int N, int V, const float* nats, const int32_t* targets, const int32_t* token_bytes,
+                      double* sum_nats, int64_t* sum_bytes, hipStream_t s);
