@@ -98,13 +98,24 @@ def make_config(cfg) -> GptConfigC:
                       float(cfg.rope_base), float(cfg.eps), 1 if cfg.dtype == "bf16" else 0)
 
 
-def _p(t) -> Optional[int]:
+def _p(t, want=None) -> Optional[int]:
+    """Device pointer of a contiguous tensor (None passes through).  `want`
+    names the element type the C side reads or writes: "f32", "f64", "i32",
+    "i64", or a GptConfigC for the configuration's storage type."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
     if not t.is_contiguous():
         raise ValueError("tensors passed to gptmi must be contiguous")
+    if want is not None:
+        import torch
+        if isinstance(want, GptConfigC):
+            exp = torch.bfloat16 if want.dtype == 1 else torch.float32
+        else:
+            exp = {"f32": torch.float32, "f64": torch.float64, "i32": torch.int32, "i64": torch.int64}[want]
+        if t.dtype != exp:
+            raise TypeError(f"gptmi expects a {exp} tensor here, got {t.dtype}")
     return t.data_ptr()
 
 
@@ -124,8 +135,8 @@ def _check(status: int):
         raise GptError(status, lib().gpt_last_error().decode())
 
 
-def _block_struct(cls, d: dict):
-    return cls(*[_p(d.get(f)) for f in BLOCK_FIELDS])
+def _block_struct(cls, d: dict, want=None):
+    return cls(*[_p(d.get(f), want) for f in BLOCK_FIELDS])
 
 
 # ----------------------------------------------------------------------------
@@ -141,35 +152,40 @@ def gpt_workspace_bytes(cfg: GptConfigC, B: int, T: int) -> int:
 
 
 def gpt_block_fwd(cfg, B, T, x, w: dict, y, saved, ws, stream=None):
-    W = _block_struct(BlockWeightsC, w)
-    _check(lib().gpt_block_fwd(ctypes.byref(cfg), B, T, _p(x), ctypes.byref(W), _p(y), _p(saved), _p(ws),
+    W = _block_struct(BlockWeightsC, w, cfg)
+    _check(lib().gpt_block_fwd(ctypes.byref(cfg), B, T, _p(x, cfg), ctypes.byref(W), _p(y, cfg), _p(saved), _p(ws),
                                _nbytes(ws), _stream(stream)))
 
 
 def gpt_block_bwd(cfg, B, T, x, dy, w: dict, saved, dx, grads: dict, accumulate, ws, stream=None):
-    W = _block_struct(BlockWeightsC, w)
-    G = _block_struct(BlockGradsC, grads)
-    _check(lib().gpt_block_bwd(ctypes.byref(cfg), B, T, _p(x), _p(dy), ctypes.byref(W), _p(saved), _p(dx),
+    W = _block_struct(BlockWeightsC, w, cfg)
+    G = _block_struct(BlockGradsC, grads, "f32")
+    _check(lib().gpt_block_bwd(ctypes.byref(cfg), B, T, _p(x, cfg), _p(dy, cfg), ctypes.byref(W), _p(saved),
+                               _p(dx, cfg),
                                ctypes.byref(G), int(accumulate), _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def lm_head_xent_fwd_bwd(cfg, N, h, W, targets, loss_scale, loss, nats, dh, dW, accumulate, ws, stream=None):
-    _check(lib().lm_head_xent_fwd_bwd(ctypes.byref(cfg), N, _p(h), _p(W), _p(targets), float(loss_scale), _p(loss),
-                                      _p(nats), _p(dh), _p(dW), int(accumulate), _p(ws), _nbytes(ws),
+    _check(lib().lm_head_xent_fwd_bwd(ctypes.byref(cfg), N, _p(h, cfg), _p(W, cfg), _p(targets, "i32"),
+                                      float(loss_scale), _p(loss, "f32"), _p(nats, "f32"), _p(dh, cfg),
+                                      _p(dW, "f32"), int(accumulate), _p(ws), _nbytes(ws),
                                       _stream(stream)))
 
 
 def val_bpb_reduce(N, nats, targets, token_bytes, V, sum_nats, sum_bytes, stream=None):
-    _check(lib().val_bpb_reduce(N, _p(nats), _p(targets), _p(token_bytes), V, _p(sum_nats), _p(sum_bytes),
+    _check(lib().val_bpb_reduce(N, _p(nats, "f32"), _p(targets, "i32"), _p(token_bytes, "i32"), V,
+                                _p(sum_nats, "f64"), _p(sum_bytes, "i64"),
                                 _stream(stream)))
 
 
 def gpt_embed_fwd(cfg, B, T, ids, wte, wpe, x0, stream=None):
-    _check(lib().gpt_embed_fwd(ctypes.byref(cfg), B, T, _p(ids), _p(wte), _p(wpe), _p(x0), _stream(stream)))
+    _check(lib().gpt_embed_fwd(ctypes.byref(cfg), B, T, _p(ids, "i32"), _p(wte, cfg), _p(wpe, cfg), _p(x0, cfg),
+                               _stream(stream)))
 
 
 def gpt_embed_bwd(cfg, B, T, ids, dx0, dwte, dwpe, accumulate, ws, stream=None):
-    _check(lib().gpt_embed_bwd(ctypes.byref(cfg), B, T, _p(ids), _p(dx0), _p(dwte), _p(dwpe), int(accumulate),
+    _check(lib().gpt_embed_bwd(ctypes.byref(cfg), B, T, _p(ids, "i32"), _p(dx0, cfg), _p(dwte, "f32"),
+                               _p(dwpe, "f32"), int(accumulate),
                                _p(ws), _nbytes(ws), _stream(stream)))
 
 
@@ -189,9 +205,11 @@ def gpt_trace_end() -> dict:
 
 
 def gpt_norm_fwd(cfg, N, x, w, b, y, stats, stream=None):
-    _check(lib().gpt_norm_fwd(ctypes.byref(cfg), N, _p(x), _p(w), _p(b), _p(y), _p(stats), _stream(stream)))
+    _check(lib().gpt_norm_fwd(ctypes.byref(cfg), N, _p(x, cfg), _p(w, cfg), _p(b, cfg), _p(y, cfg), _p(stats, "f32"),
+                              _stream(stream)))
 
 
 def gpt_norm_bwd(cfg, N, x, w, dy, resid, dx, dw, db, accumulate, ws, stream=None):
-    _check(lib().gpt_norm_bwd(ctypes.byref(cfg), N, _p(x), _p(w), _p(dy), _p(resid), _p(dx), _p(dw), _p(db),
+    _check(lib().gpt_norm_bwd(ctypes.byref(cfg), N, _p(x, cfg), _p(w, cfg), _p(dy, cfg), _p(resid, cfg), _p(dx, cfg),
+                              _p(dw, "f32"), _p(db, "f32"),
                               int(accumulate), _p(ws), _nbytes(ws), _stream(stream)))

@@ -38,6 +38,20 @@ __device__ __forceinline__ bf16x8 u22_bf8(uint2 lo, uint2 hi) {
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 __device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Raw buffer loads over one (batch, head) slice: rows at or beyond the
+// record count read as zeros, so tile loads need no branches.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// rsrc over rows [0, T) of a [T][ld] bf16 slice whose rows hold D used elements
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base, int T, long ld, int D) {
+  return make_rsrc(base, ((long)(T - 1) * ld + D) * 2);
+}
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -70,13 +84,13 @@ struct RowTile {
   static constexpr int UNITS = 64 * KU;
   static constexpr int PER = UNITS / 256;
   uint4 v[PER];
-  // src row r is at base + r * ld; rows >= nvalid are zero
-  __device__ __forceinline__ void load(const bf16* base, long ld, int nvalid) {
+  // rows r0 .. r0 + 63 of the slice; rows >= T read as zeros
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = threadIdx.x + 256 * i;
-      const int r = u / KU, c = u % KU;
-      v[i] = (r < nvalid) ? ld16(base + (long)r * ld + 8 * c) : make_uint4(0, 0, 0, 0);
+      const int r = r0 + u / KU, c = u % KU;
+      v[i] = bload(rs, r < T ? (uint32_t)(((long)r * ld + 8 * c) * 2) : OOB);
     }
   }
   __device__ __forceinline__ void store(uint4* s) const {
@@ -89,36 +103,46 @@ struct RowTile {
   }
 };
 
+// One load, both layouts: thread t < 16 * KU loads rows 4 rg .. 4 rg + 3
+// (rg = t / KU) of 16-byte column unit c = t % KU, then writes them to a row
+// tile (four 16-byte units) and/or a transposed tile (eight 8-byte units,
+// one per column, each holding the 4 rows).
 template <int D>
-struct TrTile {
-  static constexpr int NSUB = 8 * (D / 8);  // 8 row-groups x D/8 column groups
-  uint4 v[8];
-  // thread t < NSUB: row group kg = t & 7 (rows 8kg..8kg+7), col group dg = t >> 3
-  __device__ __forceinline__ void load(const bf16* base, long ld, int nvalid) {
+struct DualTile {
+  static constexpr int KU = D / 8;
+  static constexpr int NT = 16 * KU;
+  uint4 v[4];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
     const int t = threadIdx.x;
-    if (t >= NSUB) return;
-    const int kg = t & 7, dg = t >> 3;
+    if (t >= NT) return;
+    const int rg = t / KU, c = t % KU;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 8 * kg + j;
-      v[j] = (r < nvalid) ? ld16(base + (long)r * ld + 8 * dg) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + 4 * rg + j;
+      v[j] = bload(rs, r < T ? (uint32_t)(((long)r * ld + 8 * c) * 2) : OOB);
     }
   }
-  __device__ __forceinline__ void store(uint2* s) const {
+  __device__ __forceinline__ void store_row(uint4* s) const {
     const int t = threadIdx.x;
-    if (t >= NSUB) return;
-    const int kg = t & 7, dg = t >> 3;
+    if (t >= NT) return;
+    const int rg = t / KU, c = t % KU;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * rg + j;
+      s[r * KU + (c ^ (r & 7))] = v[j];
+    }
+  }
+  __device__ __forceinline__ void store_tr(uint2* s) const {
+    const int t = threadIdx.x;
+    if (t >= NT) return;
+    const int rg = t / KU, c = t % KU;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = 8 * dg + e;
-      const int sw = (d >> 1) & 15;
-      uint2 a, b;
+      const int d = 8 * c + e;
+      uint2 a;
       a.x = elem16(v[0], e) | (elem16(v[1], e) << 16);
       a.y = elem16(v[2], e) | (elem16(v[3], e) << 16);
-      b.x = elem16(v[4], e) | (elem16(v[5], e) << 16);
-      b.y = elem16(v[6], e) | (elem16(v[7], e) << 16);
-      s[d * 16 + ((2 * kg) ^ sw)] = a;
-      s[d * 16 + ((2 * kg + 1) ^ sw)] = b;
+      s[d * 16 + (rg ^ ((d >> 1) & 15))] = a;
     }
   }
 };
@@ -157,10 +181,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   const int qw = q0 + 32 * wave;
   const int qi = qw + li;
 
+  const __amdgpu_buffer_rsrc_t rQ = slice_rsrc(Qg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(Kg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(Vg, T, ld, D);
   bf16x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
-    qf[s] = u4_bf8(qi < T ? ld16(Qg + (long)qi * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+    qf[s] = u4_bf8(bload(rQ, qi < T ? (uint32_t)(((long)qi * ld + 16 * s + 8 * hf) * 2) : OOB));
 
   f32x16 acc[DT];
 #pragma unroll
@@ -172,11 +199,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
   RowTile<D> stK;
-  TrTile<D> stV;
-  stK.load(Kg, ld, T);
-  stV.load(Vg, ld, T);
+  DualTile<D> stV;
+  stK.load(rK, ld, 0, T);
+  stV.load(rV, ld, 0, T);
   stK.store(sK[0]);
-  stV.store(sV[0]);
+  stV.store_tr(sV[0]);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -184,8 +211,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
-      stK.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
-      stV.load(Vg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+      stK.load(rK, ld, kv0 + 64, T);
+      stV.load(rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
       f32x16 st[2];
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
     }
     if (more) {
       stK.store(sK[cur ^ 1]);
-      stV.store(sV[cur ^ 1]);
+      stV.store_tr(sV[cur ^ 1]);
     }
     __syncthreads();
   }
@@ -295,11 +322,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
   const int kw = k0 + 32 * wave;
   const int kj = kw + li;
 
+  const __amdgpu_buffer_rsrc_t rQ = slice_rsrc(Qg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(Kg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(Vg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rO = slice_rsrc(dOg, T, C, D);
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    kf[s] = u4_bf8(kj < T ? ld16(Kg + (long)kj * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
-    vf[s] = u4_bf8(kj < T ? ld16(Vg + (long)kj * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+    const uint32_t off = kj < T ? (uint32_t)(((long)kj * ld + 16 * s + 8 * hf) * 2) : OOB;
+    kf[s] = u4_bf8(bload(rK, off));
+    vf[s] = u4_bf8(bload(rV, off));
   }
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -309,20 +341,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
 
   const int t_begin = k0 / 64;
   const int t_end = (T + 63) / 64;
-  RowTile<D> stQ, stdO;
-  TrTile<D> stQt, stdOt;
+  DualTile<D> stQ, stdO;
   auto stage_load = [&](int t) {
     const int qt0 = t * 64;
-    stQ.load(Qg + (long)qt0 * ld, ld, T - qt0);
-    stdO.load(dOg + (long)qt0 * C, C, T - qt0);
-    stQt.load(Qg + (long)qt0 * ld, ld, T - qt0);
-    stdOt.load(dOg + (long)qt0 * C, C, T - qt0);
+    stQ.load(rQ, ld, qt0, T);
+    stdO.load(rO, C, qt0, T);
   };
   auto stage_store = [&](int t, int buf) {
-    stQ.store(sQ[buf]);
-    stdO.store(sdO[buf]);
-    stQt.store(sQt[buf]);
-    stdOt.store(sdOt[buf]);
+    stQ.store_row(sQ[buf]);
+    stQ.store_tr(sQt[buf]);
+    stdO.store_row(sdO[buf]);
+    stdO.store_tr(sdOt[buf]);
     const int qt0 = t * 64;
     if (threadIdx.x < 64) {
       const int q = qt0 + threadIdx.x;
@@ -439,11 +468,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   const int qw = q0 + 32 * wave;
   const int qi = qw + li;
 
+  const __amdgpu_buffer_rsrc_t rQ = slice_rsrc(Qg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(Kg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(Vg, T, ld, D);
+  const __amdgpu_buffer_rsrc_t rO = slice_rsrc(dOg, T, C, D);
   bf16x8 qf[KS], df[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    qf[s] = u4_bf8(qi < T ? ld16(Qg + (long)qi * ld + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
-    df[s] = u4_bf8(qi < T ? ld16(dOg + (long)qi * C + 16 * s + 8 * hf) : make_uint4(0, 0, 0, 0));
+    qf[s] = u4_bf8(bload(rQ, qi < T ? (uint32_t)(((long)qi * ld + 16 * s + 8 * hf) * 2) : OOB));
+    df[s] = u4_bf8(bload(rO, qi < T ? (uint32_t)(((long)qi * C + 16 * s + 8 * hf) * 2) : OOB));
   }
   const long row_lse = ((long)b * H + h) * T + qi;
   const float L2 = qi < T ? lse[row_lse] * LOG2E : 0.0f;
@@ -456,23 +489,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D> stK, stV;
-  TrTile<D> stKt;
-  stK.load(Kg, ld, T);
-  stV.load(Vg, ld, T);
-  stKt.load(Kg, ld, T);
-  stK.store(sK[0]);
+  DualTile<D> stK;
+  RowTile<D> stV;
+  stK.load(rK, ld, 0, T);
+  stV.load(rV, ld, 0, T);
+  stK.store_row(sK[0]);
+  stK.store_tr(sKt[0]);
   stV.store(sV[0]);
-  stKt.store(sKt[0]);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
-      stK.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
-      stV.load(Vg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
-      stKt.load(Kg + (long)(kv0 + 64) * ld, ld, T - kv0 - 64);
+      stK.load(rK, ld, kv0 + 64, T);
+      stV.load(rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
       f32x16 St[2], dPt[2];
@@ -511,9 +542,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
       }
     }
     if (more) {
-      stK.store(sK[cur ^ 1]);
+      stK.store_row(sK[cur ^ 1]);
+      stK.store_tr(sKt[cur ^ 1]);
       stV.store(sV[cur ^ 1]);
-      stKt.store(sKt[cur ^ 1]);
     }
     __syncthreads();
   }

@@ -66,14 +66,32 @@ template <> struct Vec8<float> {
   }
 };
 
-// Exact-erf GELU and its derivative (ROCm device erff / expf).
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0 (odd extension), |error| <= 1.5e-7.
+// Inline arithmetic (one exp, one reciprocal) so GEMM epilogues make no calls.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __expf(-ax * ax);
+  const float r = fmaf(-poly, e, 1.0f);
+  return copysignf(r, x);
+}
+
+// GELU with the exact (erf) form, u * Phi(u), and its derivative
+// Phi(u) + u * phi(u).
 __device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f));
 }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-  float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-  return cdf + u * pdf;
+  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f));
+  const float pdf = __expf(-0.5f * u * u) * 0.39894228040143268f;
+  return fmaf(u, pdf, cdf);
 }
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }

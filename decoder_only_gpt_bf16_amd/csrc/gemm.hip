@@ -51,63 +51,76 @@ __device__ __forceinline__ void store4(T* p, const float* f) {
   }
 }
 
-// Elementwise epilogue for 4 consecutive columns n..n+3 of row m.
-template <typename T, int EPI>
-__device__ __forceinline__ void epi4(const GemmParams& p, int m, int n, float* v) {
+template <typename T, int W>
+__device__ __forceinline__ void loadW(const T* p, float* f) {
+  if constexpr (W == 8) {
+    Vec8<T>::load(p, f);
+  } else {
+    load4<T>(p, f);
+  }
+}
+template <typename T, int W>
+__device__ __forceinline__ void storeW(T* p, const float* f) {
+  if constexpr (W == 8) {
+    Vec8<T>::store(p, f);
+  } else {
+    store4<T>(p, f);
+  }
+}
+
+// Elementwise epilogue for W consecutive columns n..n+W-1 of row m.  Partial
+// vectors (n + W > N) take the same arithmetic with guarded element access.
+template <typename T, int EPI, int W>
+__device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v) {
   if (m >= p.M || n >= p.N) return;
-  const bool full = (n + 4 <= p.N);
-  float t[4];
+  const bool full = (n + W <= p.N);
+  float t[W];
   if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
     if (p.bias) {
       const T* b = reinterpret_cast<const T*>(p.bias) + n;
-      if (full) { load4<T>(b, t); for (int e = 0; e < 4; ++e) v[e] += t[e]; }
-      else for (int e = 0; e < 4; ++e) if (n + e < p.N) v[e] += to_f32(b[e]);
+      if (full) loadW<T, W>(b, t);
+      else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(b[e]) : 0.0f;
+      for (int e = 0; e < W; ++e) v[e] += t[e];
     }
   }
   if constexpr (EPI == EPI_STORE) {
     if (p.resid) {
       const T* r = reinterpret_cast<const T*>(p.resid) + (long)m * p.ldr + n;
-      if (full) { load4<T>(r, t); for (int e = 0; e < 4; ++e) v[e] += t[e]; }
-      else for (int e = 0; e < 4; ++e) if (n + e < p.N) v[e] += to_f32(r[e]);
+      if (full) loadW<T, W>(r, t);
+      else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(r[e]) : 0.0f;
+      for (int e = 0; e < W; ++e) v[e] += t[e];
     }
-    T* o = reinterpret_cast<T*>(p.out) + (long)m * p.ldc + n;
-    if (full) store4<T>(o, v);
-    else for (int e = 0; e < 4; ++e) if (n + e < p.N) o[e] = from_f32<T>(v[e]);
   } else if constexpr (EPI == EPI_GELU) {
-    float g[4];
-    for (int e = 0; e < 4; ++e) g[e] = gelu_f(v[e]);
-    T* o = reinterpret_cast<T*>(p.out) + (long)m * p.ldc + n;
+    float g[W];
+    for (int e = 0; e < W; ++e) g[e] = gelu_f(v[e]);
     T* o2 = reinterpret_cast<T*>(p.out2) + (long)m * p.ldc + n;
-    if (full) { store4<T>(o, v); store4<T>(o2, g); }
-    else for (int e = 0; e < 4; ++e) if (n + e < p.N) { o[e] = from_f32<T>(v[e]); o2[e] = from_f32<T>(g[e]); }
+    if (full) storeW<T, W>(o2, g);
+    else for (int e = 0; e < W; ++e) if (n + e < p.N) o2[e] = from_f32<T>(g[e]);
   } else if constexpr (EPI == EPI_GELU_BWD) {
     const T* u = reinterpret_cast<const T*>(p.aux) + (long)m * p.ldaux + n;
-    T* o = reinterpret_cast<T*>(p.out) + (long)m * p.ldc + n;
-    if (full) {
-      load4<T>(u, t);
-      for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(t[e]);
-      store4<T>(o, v);
-    } else {
-      for (int e = 0; e < 4; ++e) if (n + e < p.N) o[e] = from_f32<T>(v[e] * gelu_grad_f(to_f32(u[e])));
-    }
-  } else if constexpr (EPI == EPI_F32) {
-    float* o = reinterpret_cast<float*>(p.out) + (long)blockIdx.z * p.split_stride + (long)m * p.ldc + n;
-    if (full && (p.ldc & 3) == 0) {
-      if (p.accumulate) { load4<float>(o, t); for (int e = 0; e < 4; ++e) v[e] += t[e]; }
-      store4<float>(o, v);
-    } else {
-      for (int e = 0; e < 4; ++e) if (n + e < p.N) o[e] = p.accumulate ? o[e] + v[e] : v[e];
-    }
+    if (full) loadW<T, W>(u, t);
+    else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(u[e]) : 0.0f;
+    for (int e = 0; e < W; ++e) v[e] *= gelu_grad_f(t[e]);
   } else if constexpr (EPI == EPI_XENT_GRAD) {
     const float l = p.lse[m];
     const int tg = p.tgt[m] - p.col_offset;
-    for (int e = 0; e < 4; ++e) {
-      float pr = exp2f((v[e] - l) * LOG2E);
+    for (int e = 0; e < W; ++e) {
+      const float pr = exp2f((v[e] - l) * LOG2E);
       v[e] = (pr - (n + e == tg ? 1.0f : 0.0f)) * p.scale;
     }
+  }
+  if constexpr (EPI == EPI_F32) {
+    float* o = reinterpret_cast<float*>(p.out) + (long)blockIdx.z * p.split_stride + (long)m * p.ldc + n;
+    if (full && (p.ldc & 3) == 0) {
+      if (p.accumulate) { loadW<float, W>(o, t); for (int e = 0; e < W; ++e) v[e] += t[e]; }
+      storeW<float, W>(o, v);
+    } else {
+      for (int e = 0; e < W; ++e) if (n + e < p.N) o[e] = p.accumulate ? o[e] + v[e] : v[e];
+    }
+  } else {
     T* o = reinterpret_cast<T*>(p.out) + (long)m * p.ldc + n;
-    if (full) store4<T>(o, v);
-    else for (int e = 0; e < 4; ++e) if (n + e < p.N) o[e] = from_f32<T>(v[e]);
+    if (full) storeW<T, W>(o, v);
+    else for (int e = 0; e < W; ++e) if (n + e < p.N) o[e] = from_f32<T>(v[e]);
   }
 }
 
@@ -131,32 +144,35 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 }
 
 // ------------------------------------------------------------ staging
+// Operands are read with raw buffer loads: a lane whose 16-byte vector lies
+// outside the matrix (row >= rows, k >= kend) gets an offset beyond the
+// buffer's record count and the hardware returns zeros, so the loads carry
+// no branches and stay in flight together.  Extents along the contiguous
+// dimension are multiples of 8 elements (checked on the host).
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Operand with k contiguous in HBM: R rows x 64 k, thread t covers unit
 // c = t & 7 of rows (t >> 3) + 32 i.
 template <int R>
 struct StageKc {
   static constexpr int NV = R / 32;
   uint4 v[NV];
-  __device__ __forceinline__ void load(const bf16* X, long ld, int r0, int rmax, int k0, int kend) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax, int k0, int kend) {
     const int t = threadIdx.x;
-    const int c = t & 7;
-    const int kk = k0 + 8 * c;
+    const int kk = k0 + 8 * (t & 7);
+    const bool kok = kk + 8 <= kend;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int gr = r0 + (t >> 3) + 32 * i;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (gr < rmax) {
-        const bf16* src = X + (long)gr * ld + kk;
-        if (kk + 8 <= kend) {
-          u = *reinterpret_cast<const uint4*>(src);
-        } else if (kk < kend) {
-          uint16_t h[8];
-          for (int e = 0; e < 8; ++e)
-            h[e] = (kk + e < kend) ? reinterpret_cast<const uint16_t*>(src)[e] : (uint16_t)0;
-          u = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
-        }
-      }
-      v[i] = u;
+      const uint32_t off = (kok && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
+      v[i] = bload(rs, off);
     }
   }
   __device__ __forceinline__ void store(uint4* lds) const {
@@ -176,29 +192,19 @@ template <int R>
 struct StageKm {
   static constexpr int NS = (R + 255) / 256;
   uint4 v[NS][8];
-  __device__ __forceinline__ void load(const bf16* X, long ld, int r0, int rmax, int k0, int kend) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax, int k0, int kend) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int s = t + 256 * i;
       const int kg = s & 7, rg = s >> 3;
       const int gr = r0 + 8 * rg;
+      const bool rok = s < R && gr + 8 <= rmax;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int gk = k0 + 8 * kg + j;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (s < R && gk < kend && gr < rmax) {
-          const bf16* src = X + (long)gk * ld + gr;
-          if (gr + 8 <= rmax) {
-            u = *reinterpret_cast<const uint4*>(src);
-          } else {
-            uint16_t h[8];
-            for (int e = 0; e < 8; ++e)
-              h[e] = (gr + e < rmax) ? reinterpret_cast<const uint16_t*>(src)[e] : (uint16_t)0;
-            u = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
-          }
-        }
-        v[i][j] = u;
+        const uint32_t off = (rok && gk < kend) ? (uint32_t)(((long)gk * ld + gr) * 2) : OOB;
+        v[i][j] = bload(rs, off);
       }
     }
   }
@@ -255,8 +261,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
   const int wm = (wave & 1) * (BM / 2);
   const int wn = (wave >> 1) * (BN / 2);
 
-  const bf16* A = reinterpret_cast<const bf16*>(p.A);
-  const bf16* B = reinterpret_cast<const bf16*>(p.B);
+  // record counts: rows x leading dimension of each operand, in bytes
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -269,8 +276,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
   Stage<A_KMAJ, BM> sa;
   Stage<B_KMAJ, BN> sb;
   if (nk > 0) {
-    sa.load(A, p.lda, m0, p.M, kbeg, kend);
-    sb.load(B, p.ldb, n0, p.N, kbeg, kend);
+    sa.load(ra, p.lda, m0, p.M, kbeg, kend);
+    sb.load(rb, p.ldb, n0, p.N, kbeg, kend);
     sa.store(lds);
     sb.store(lds + BM * 8);
   }
@@ -283,24 +290,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
     const bool more = kt + 1 < nk;
     if (more) {
       const int k0 = kbeg + (kt + 1) * BK;
-      sa.load(A, p.lda, m0, p.M, k0, kend);
-      sb.load(B, p.ldb, n0, p.N, k0, kend);
+      sa.load(ra, p.lda, m0, p.M, k0, kend);
+      sb.load(rb, p.ldb, n0, p.N, k0, kend);
     }
     const uint4* As = lds + cur * STAGE_UNITS;
     const uint4* Bs = As + BM * 8;
+    // fragments of k-step kk+1 are read while the MFMAs of step kk run
+    bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = as_bf16x8(As[(wm + 32 * i + lrow) * 8 + (lhalf ^ (lrow & 7))]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = as_bf16x8(Bs[(wn + 32 * j + lrow) * 8 + (lhalf ^ (lrow & 7))]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int unit = (2 * kk + lhalf) ^ (lrow & 7);
-      bf16x8 af[TM], bfr[TN];
+      const int cb = kk & 1;
+      if (kk + 1 < BK / 16) {
+        const int unit = (2 * (kk + 1) + lhalf) ^ (lrow & 7);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = as_bf16x8(As[(wm + 32 * i + lrow) * 8 + unit]);
+        for (int i = 0; i < TM; ++i) af[cb ^ 1][i] = as_bf16x8(As[(wm + 32 * i + lrow) * 8 + unit]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = as_bf16x8(Bs[(wn + 32 * j + lrow) * 8 + unit]);
+        for (int j = 0; j < TN; ++j) bfr[cb ^ 1][j] = as_bf16x8(Bs[(wn + 32 * j + lrow) * 8 + unit]);
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
     }
     if (more) {
       uint4* nxt = lds + (cur ^ 1) * STAGE_UNITS;
@@ -310,57 +325,60 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
     __syncthreads();
   }
 
-  // lane holds row m = m0 + wm + 32 i + lrow and columns
-  // n = n0 + wn + 32 j + 8 g + 4 lhalf + e (register 4 g + e).
-  if constexpr (EPI == EPI_XENT_STATS) {
-    const int nbase = n0 + wn;
+  // Epilogue through LDS (free after the loop's last barrier): each wave
+  // writes one 32-row strip of its accumulators (lane: row lrow, columns
+  // 32 j + 8 g + 4 lhalf + e) and reads it back as 8-column row vectors, so
+  // global reads and writes of the epilogue are contiguous 16-byte vectors.
+  constexpr int WN = BN / 2;              // columns per wave
+  constexpr int PITCH = WN + 4;           // floats per staged row
+  constexpr int LPR = WN / 8;             // lanes per row in the read-back
+  constexpr int RPP = 64 / LPR;           // rows per pass
+  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm + 32 * i + lrow;
-      const int tg = (m < p.M) ? p.tgt[m] - p.col_offset : -1;
-      float mx = -INFINITY, zt = 0.0f;
-      bool have = false;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = nbase + 32 * j + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-          const float v = acc[j][i][r];
-          if (n < p.N) mx = fmaxf(mx, v);
-          if (n == tg) { zt = v; have = true; }
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float s = 0.0f;
-      if (mx != -INFINITY) {
-        const float ms = mx * LOG2E;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int n = nbase + 32 * j + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-            if (n < p.N) s += exp2f(fmaf(acc[j][i][r], LOG2E, -ms));
-          }
-      }
-      s += __shfl_xor(s, 32, 64);
-      if (m < p.M) {
-        if (have) p.ztgt[m] = zt;
-        if (lhalf == 0) p.part[(long)m * p.part_ld + p.part_off + nbase / (BN / 2)] = make_float2(mx, s);
-      }
-    }
-  } else {
-    using OutT = bf16;
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm + 32 * i + lrow;
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(ep + lrow * PITCH + 32 * j + 8 * g + 4 * lhalf) =
+            make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+    __builtin_amdgcn_wave_barrier();
+    const int col = (lane % LPR) * 8;
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int row = pass * RPP + lane / LPR;
+      float v[8];
+      const float4 a = *reinterpret_cast<const float4*>(ep + row * PITCH + col);
+      const float4 b = *reinterpret_cast<const float4*>(ep + row * PITCH + col + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      const int m = m0 + wm + 32 * i + row;
+      const int n = n0 + wn + col;
+      if constexpr (EPI == EPI_XENT_STATS) {
+        // (max, sum exp) of this row over the wave's WN columns; LPR lanes share a row
+        const int tg = (m < p.M) ? p.tgt[m] - p.col_offset : -1;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn + 32 * j + 8 * g + 4 * lhalf;
-          float v[4] = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
-          epi4<OutT, EPI>(p, m, n, v);
+        for (int e = 0; e < 8; ++e) {
+          if (n + e < p.N) mx = fmaxf(mx, v[e]);
+          if (n + e == tg) p.ztgt[m] = v[e];
         }
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float sm = 0.0f;
+        if (mx != -INFINITY) {
+          const float ms = mx * LOG2E;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < p.N) sm += exp2f(fmaf(v[e], LOG2E, -ms));
+        }
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
+        if (m < p.M && lane % LPR == 0)
+          p.part[(long)m * p.part_ld + p.part_off + (n0 + wn) / WN] = make_float2(mx, sm);
+      } else {
+        epiW<bf16, EPI, 8>(p, m, n, v);
       }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -411,7 +429,7 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-    epi4<T, EPI>(p, m0 + ty * 4 + i, n0 + tx * 4, v);
+    epiW<T, EPI, 4>(p, m0 + ty * 4 + i, n0 + tx * 4, v);
   }
 }
 
@@ -487,20 +505,40 @@ int xent_part_cols() { return 128; }
 
 size_t gemm_split_scratch_bytes(const GemmDesc& d, int dtype) {
   if (dtype != 1 || d.epi != EPI_F32) return 0;
+  // sizes only: the MFMA path may take any such problem
   Plan pl = plan_mfma(d);
   if (pl.splits <= 1) return 0;
   return align256((size_t)pl.splits * d.M * d.N * sizeof(float));
 }
 
+// Extent in bytes of an operand stored [rows][ld] whose last row is read up
+// to `cols` elements; 0 if the MFMA path cannot take it (the contiguous
+// extent or leading dimension is not a multiple of 8, the base is not
+// 16-byte aligned, or offsets would not fit the 31-bit buffer range).
+static uint32_t operand_bytes(const void* p, long rows, long ld, long cols) {
+  if (rows <= 0 || cols % 8 || ld % 8 || (reinterpret_cast<uintptr_t>(p) & 15)) return 0;
+  const long bytes = ((rows - 1) * ld + cols) * 2;
+  if (bytes <= 0 || bytes >= (1L << 31)) return 0;
+  return (uint32_t)bytes;
+}
+
+static bool mfma_ok(const GemmDesc& d, uint32_t& ab, uint32_t& bb) {
+  ab = d.a_kmaj ? operand_bytes(d.A, d.K, d.lda, d.M) : operand_bytes(d.A, d.M, d.lda, d.K);
+  bb = d.b_kmaj ? operand_bytes(d.B, d.K, d.ldb, d.N) : operand_bytes(d.B, d.N, d.ldb, d.K);
+  return ab && bb && d.K > 0;
+}
+
 hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return hipSuccess;
   GemmParams p = make_params(d);
-  if (dtype == 1) {
+  uint32_t ab = 0, bb = 0;
+  if (dtype == 1 && mfma_ok(d, ab, bb)) {
     Plan pl = plan_mfma(d);
     p.tiles_m = cdiv(d.M, pl.BMv);
     p.tiles_n = cdiv(d.N, pl.BNv);
     p.k_split = pl.k_split;
-    if (d.K <= 0) { pl.splits = 1; p.k_split = 0; }
+    p.a_bytes = ab;
+    p.b_bytes = bb;
     const bool split = pl.splits > 1;
     if (split) {
       p.out = ws; p.ldc = d.N; p.accumulate = 0; p.split_stride = (long)d.M * d.N;
@@ -539,6 +577,14 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
       e = hipGetLastError();
     }
     return e;
+  }
+  if (dtype == 1) {
+    // bf16 operands the MFMA path cannot take (odd extents): SIMT kernel
+    p.k_split = d.K > 0 ? d.K : 0;
+    const bool ak = d.a_kmaj, bk = d.b_kmaj;
+    if (d.epi == EPI_F32 && ak && bk) return go_simt<bf16, true, true, EPI_F32>(p, 1, s);
+    if (d.epi == EPI_F32 && !ak && bk) return go_simt<bf16, false, true, EPI_F32>(p, 1, s);
+    return hipErrorInvalidValue;
   }
   // fp32 storage: SIMT kernel, no split.
   p.k_split = d.K > 0 ? d.K : 0;

@@ -29,6 +29,7 @@ struct GemmParams {
   int M, N, K;
   int k_split;            // K elements handled per blockIdx.z
   int tiles_m, tiles_n;
+  uint32_t a_bytes, b_bytes;  // bytes of A and B covered by their buffer loads
   // epilogue
   void* out;
   long ldc;

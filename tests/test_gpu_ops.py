@@ -39,13 +39,13 @@ def test_lm_head_xent(dtype, N, C, V):
     h = synth.round_to(rng.standard_normal((N, C)), dtype)
     W = synth.round_to(0.05 * rng.standard_normal((V, C)), dtype)
     y = rng.integers(0, V, N)
-    cfg = _cfg(dtype, V, C)
+    cfg = _cfg(dtype, V, C, H=C // 64 if C >= 64 else 1)
     c = B.make_config(cfg)
     ws = workspace(c, 1, N)
     dh = torch.empty((N, C), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
     dW = torch.full((V, C), 7.0, dtype=torch.float32, device="cuda")
-    loss = torch.zeros(1, device="cuda")
-    nats = torch.zeros(N, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nats = torch.zeros(N, dtype=torch.float32, device="cuda")
     B.lm_head_xent_fwd_bwd(c, N, upload(h, dtype), upload(W, dtype), upload_i32(y), 1.0 / N, loss, nats, dh, dW, 0,
                            ws)
     torch.cuda.synchronize()
@@ -56,7 +56,7 @@ def test_lm_head_xent(dtype, N, C, V):
     assert_rel("dh", to_f64(dh), dh_ref, REL_ACT, rep)
     assert_rel("dW", to_f64(dW), dW_ref, REL_ACT, rep)
     # forward only leaves dW alone and gives the same loss
-    loss2 = torch.zeros(1, device="cuda")
+    loss2 = torch.zeros(1, dtype=torch.float32, device="cuda")
     B.lm_head_xent_fwd_bwd(c, N, upload(h, dtype), upload(W, dtype), upload_i32(y), 1.0 / N, loss2, None, None, None,
                            0, ws)
     torch.cuda.synchronize()
@@ -72,8 +72,8 @@ def test_xent_uniform_logits_give_ln_V():
     ws = workspace(c, 1, N)
     h = upload(synth.round_to(np.random.default_rng(0).standard_normal((N, C)), "bf16"), "bf16")
     W = torch.zeros((V, C), dtype=torch.bfloat16, device="cuda")
-    loss = torch.zeros(1, device="cuda")
-    nats = torch.zeros(N, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nats = torch.zeros(N, dtype=torch.float32, device="cuda")
     y = upload_i32(np.arange(N) * 500)
     B.lm_head_xent_fwd_bwd(c, N, h, W, y, 1.0 / N, loss, nats, None, None, 0, ws)
     torch.cuda.synchronize()
@@ -130,8 +130,8 @@ def test_embed_fwd_bwd(dtype, rope, zipf):
     x0 = torch.empty((Bsz * T, C), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
     B.gpt_embed_fwd(c, Bsz, T, upload_i32(ids), upload(wte, dtype), upload(wpe, dtype), x0)
     ws = workspace(c, Bsz, T)
-    dwte = torch.full((V, C), 3.0, device="cuda")
-    dwpe = None if rope else torch.full((512, C), 3.0, device="cuda")
+    dwte = torch.full((V, C), 3.0, dtype=torch.float32, device="cuda")
+    dwpe = None if rope else torch.full((512, C), 3.0, dtype=torch.float32, device="cuda")
     B.gpt_embed_bwd(c, Bsz, T, upload_i32(ids), upload(dx0.reshape(-1, C), dtype), dwte, dwpe, 0, ws)
     torch.cuda.synchronize()
     x_ref = O.embed_fwd(ids, wte, wpe)
@@ -167,7 +167,7 @@ def test_embed_out_of_range_ids():
     B.gpt_embed_fwd(c, Bsz, T, upload_i32(ids), upload(wte, "bf16"), None, x0)
     dx0 = synth.round_to(rng.standard_normal((T, C)), "bf16")
     ws = workspace(c, Bsz, T)
-    dwte = torch.zeros((V, C), device="cuda")
+    dwte = torch.zeros((V, C), dtype=torch.float32, device="cuda")
     B.gpt_embed_bwd(c, Bsz, T, upload_i32(ids), upload(dx0, "bf16"), dwte, None, 0, ws)
     torch.cuda.synchronize()
     x = to_f64(x0)
@@ -191,11 +191,11 @@ def test_norm_fwd_bwd(norm, dtype):
     res = synth.round_to(rng.standard_normal((N, C)), dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     y = torch.empty((N, C), dtype=tdt, device="cuda")
-    stats = torch.empty(2 * N, device="cuda")
+    stats = torch.empty(2 * N, dtype=torch.float32, device="cuda")
     B.gpt_norm_fwd(c, N, upload(x, dtype), upload(w, dtype), upload(b, dtype), y, stats)
     dx = torch.empty_like(y)
-    dw = torch.zeros(C, device="cuda") if w is not None else None
-    db = torch.zeros(C, device="cuda") if b is not None else None
+    dw = torch.zeros(C, dtype=torch.float32, device="cuda") if w is not None else None
+    db = torch.zeros(C, dtype=torch.float32, device="cuda") if b is not None else None
     ws = workspace(c, 1, N)
     B.gpt_norm_bwd(c, N, upload(x, dtype), upload(w, dtype), upload(dy, dtype), upload(res, dtype), dx, dw, db, 0, ws)
     torch.cuda.synchronize()
