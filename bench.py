@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the GPT-2 block, GPT-2 step and d20 eval")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes); "
@@ -112,6 +114,15 @@ def main():
     from decoder_only_gpt_bf16_amd import binding as B
     from decoder_only_gpt_bf16_amd import synth
     from decoder_only_gpt_bf16_amd.model import BlockRunner
+
+    if args.copy_calibration:
+        # each copy reads 256 MiB and writes 256 MiB of HBM
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = synth.D20_BLOCK
     cfg = w.cfg

@@ -26,6 +26,8 @@
 //    is where a 32x32 accumulator keeps its rows; operands read from LDS
 //    use the same mapping.
 // SIMT kernels cover fp32 storage and other head dims (any D <= 128).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace {
@@ -34,9 +36,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ bf16x8 u4_bf8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ bf16x8 u22_bf8(uint2 lo, uint2 hi) {
-  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
 __device__ __forceinline__ uint4 ld16(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Raw buffer loads over one (batch, head) slice: rows at or beyond the
@@ -56,12 +55,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
-// element e (0..7) of a 16-byte vector of bf16, as raw 16 bits
-__device__ __forceinline__ uint32_t elem16(const uint4& v, int e) {
-  const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
 // Pack accumulator registers 4g0..4g0+3 and 4g0+4..4g0+7 of a 32x32 tile as
 // the 8 bf16 k-slots of a B operand.
 __device__ __forceinline__ bf16x8 pack_slots(const float* p, int g0) {
@@ -74,15 +67,32 @@ __device__ __forceinline__ bf16x8 pack_slots(const float* p, int g0) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile staging.  "Row" tiles: ROWS x D bf16, 16-byte unit c of row r at
-// c ^ (r & 7).  "Transposed" tiles: D x ROWS, 8-byte units of 4 rows, unit u
-// of line d at u ^ ((d >> 1) & 15); ROWS = 64 gives 16 units per line.
+// LDS tiles: 64 rows x D bf16, row-major, 16-byte unit u of row r stored at
+// u ^ f(r).  The swizzle keeps both access patterns free of bank conflicts
+// on a 64-bank LDS: 16-byte fragment reads of 16 consecutive rows, and
+// ds_read_b64_tr_b16 reads (4 aligned rows x 16 or 32 columns).
+//   256-byte rows (D = 128): f(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+//   128-byte rows (D = 64):  f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+// A tile serves as an MFMA A operand two ways:
+//   row_frag: rows of the tile, 8 consecutive columns per lane (16 ks + 8 hf);
+//   tr_frag:  columns of the tile (the transposed matrix), via the gfx950
+//             transpose read: within a 16-lane group, lane i receives element
+//             i % 4 of the 4-element vectors addressed by lanes 4k + i / 4
+//             (k = 0..3), so when those lanes address rows j0 + k at column
+//             D0 + 4 (i % 4), lane i gets rows j0..j0+3 of column D0 + i.
 // ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int upos(int r, int u) { return r * (D / 8) + (u ^ swz<D>(r)); }
+
 template <int D>
 struct RowTile {
   static constexpr int KU = D / 8;
-  static constexpr int UNITS = 64 * KU;
-  static constexpr int PER = UNITS / 256;
+  static constexpr int PER = 64 * KU / 256;
   uint4 v[PER];
   // rows r0 .. r0 + 63 of the slice; rows >= T read as zeros
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
@@ -97,66 +107,35 @@ struct RowTile {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int u = threadIdx.x + 256 * i;
-      const int r = u / KU, c = u % KU;
-      s[r * KU + (c ^ (r & 7))] = v[i];
+      s[upos<D>(u / KU, u % KU)] = v[i];
     }
   }
 };
 
-// One load, both layouts: thread t < 16 * KU loads rows 4 rg .. 4 rg + 3
-// (rg = t / KU) of 16-byte column unit c = t % KU, then writes them to a row
-// tile (four 16-byte units) and/or a transposed tile (eight 8-byte units,
-// one per column, each holding the 4 rows).
-template <int D>
-struct DualTile {
-  static constexpr int KU = D / 8;
-  static constexpr int NT = 16 * KU;
-  uint4 v[4];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
-    const int t = threadIdx.x;
-    if (t >= NT) return;
-    const int rg = t / KU, c = t % KU;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = r0 + 4 * rg + j;
-      v[j] = bload(rs, r < T ? (uint32_t)(((long)r * ld + 8 * c) * 2) : OOB);
-    }
-  }
-  __device__ __forceinline__ void store_row(uint4* s) const {
-    const int t = threadIdx.x;
-    if (t >= NT) return;
-    const int rg = t / KU, c = t % KU;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * rg + j;
-      s[r * KU + (c ^ (r & 7))] = v[j];
-    }
-  }
-  __device__ __forceinline__ void store_tr(uint2* s) const {
-    const int t = threadIdx.x;
-    if (t >= NT) return;
-    const int rg = t / KU, c = t % KU;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * c + e;
-      uint2 a;
-      a.x = elem16(v[0], e) | (elem16(v[1], e) << 16);
-      a.y = elem16(v[2], e) | (elem16(v[3], e) << 16);
-      s[d * 16 + (rg ^ ((d >> 1) & 15))] = a;
-    }
-  }
-};
-
-// A-operand fragment from a row tile: row r, k-step s (16 wide), lane half h.
+// A operand from tile rows: row r, k-step ks (columns 16 ks + 8 hf .. + 7).
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const uint4* s, int r, int ks, int hf) {
-  constexpr int KU = D / 8;
-  return u4_bf8(s[r * KU + ((2 * ks + hf) ^ (r & 7))]);
+  return u4_bf8(s[upos<D>(r, 2 * ks + hf)]);
 }
-// A-operand fragment from a transposed tile: line d, reduction step ks over 16 rows.
-__device__ __forceinline__ bf16x8 tr_frag(const uint2* s, int d, int ks, int hf) {
-  const int sw = (d >> 1) & 15;
-  return u22_bf8(s[d * 16 + ((4 * ks + hf) ^ sw)], s[d * 16 + ((4 * ks + 2 + hf) ^ sw)]);
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ i16x4 tr_read(const uint4* s, int row, int col) {
+  const bf16* base = reinterpret_cast<const bf16*>(s);
+  const int off = upos<D>(row, col >> 3) * 8 + (col & 7);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+}
+// A operand from tile columns: lane l gets column 32 dt + (l & 31) at rows
+// 16 ks + 4 hf + 0..3 (slots 0..3) and 16 ks + 8 + 4 hf + 0..3 (slots 4..7).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint4* s, int dt, int ks, int lane) {
+  const int i = lane & 15, g = lane >> 4, hf = lane >> 5;
+  const int col = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+  const int row = 16 * ks + 4 * hf + (i >> 2);
+  const i16x4 a = tr_read<D>(s, row, col);
+  const i16x4 b = tr_read<D>(s, row + 8, col);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ------------------------------------------------------------ forward (MFMA)
@@ -166,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
                                                         float scale_log2) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
-  __shared__ uint2 sV[2][D * 16];
+  __shared__ uint4 sV[2][64 * KU];
   const int nqb = (T + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -198,12 +177,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D> stK;
-  DualTile<D> stV;
+  RowTile<D> stK, stV;
   stK.load(rK, ld, 0, T);
   stV.load(rV, ld, 0, T);
   stK.store(sK[0]);
-  stV.store_tr(sV[0]);
+  stV.store(sV[0]);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -215,41 +193,58 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       stV.load(rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
+      // S^T = K Q^T for two 32-key sub-tiles; k-step s+1 fragments are read
+      // while the MFMAs of step s run
       f32x16 st[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[jt][r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sK[cur], 32 * jt + li, s, hf), qf[s],
-                                                           st[jt], 0, 0, 0);
-      }
-      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
-      float p[2][16];
-      float mx = -INFINITY;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = st[jt][r] * scale_log2;
-          if (need_mask) {
-            const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (j > qi || j >= T) x = -INFINITY;
-          }
-          p[jt][r] = x;
-          mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) st[jt][r] = 0.0f;
+      bf16x8 kfr[2][2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) kfr[0][jt] = row_frag<D>(sK[cur], 32 * jt + li, 0, hf);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) kfr[(s + 1) & 1][jt] = row_frag<D>(sK[cur], 32 * jt + li, s + 1, hf);
         }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+          st[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s & 1][jt], qf[s], st[jt], 0, 0, 0);
+      }
+      // online softmax in the log2 domain; the causal mask is applied only on
+      // tiles that cross the diagonal or the sequence end (uniform branch)
+      float p[2][16];
+      auto scores = [&](auto masked) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = st[jt][r] * scale_log2;
+            if constexpr (decltype(masked)::value) {
+              const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (j > qi || j >= T) x = -INFINITY;
+            }
+            p[jt][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        return mx;
+      };
+      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
+      float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
       const bool dead = (m_new == -INFINITY);
-      const float corr = dead ? 1.0f : exp2f(m_run - m_new);
+      const float corr = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float msub = dead ? 0.0f : m_new;
       float rs = 0.0f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = dead ? 0.0f : exp2f(p[jt][r] - m_new);
+          const float e = __builtin_amdgcn_exp2f(p[jt][r] - msub);
           p[jt][r] = e;
           rs += e;
         }
@@ -260,18 +255,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+      // O^T += V^T P^T; V^T fragments of step ks+1 are read during step ks
+      bf16x8 vfr[2][DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vfr[0][dt] = tr_frag<D>(sV[cur], dt, 0, lane);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vfr[(ks + 1) & 1][dt] = tr_frag<D>(sV[cur], dt, ks + 1, lane);
+        }
         const bf16x8 pb = pack_slots(p[ks >> 1], 2 * (ks & 1));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sV[cur], 32 * dt + li, ks, hf), pb, acc[dt],
-                                                            0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks & 1][dt], pb, acc[dt], 0, 0, 0);
       }
     }
     if (more) {
       stK.store(sK[cur ^ 1]);
-      stV.store_tr(sV[cur ^ 1]);
+      stV.store(sV[cur ^ 1]);
     }
     __syncthreads();
   }
@@ -304,8 +306,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sQ[2][64 * KU];
   __shared__ uint4 sdO[2][64 * KU];
-  __shared__ uint2 sQt[2][D * 16];
-  __shared__ uint2 sdOt[2][D * 16];
   __shared__ float sL[2][64], sDl[2][64];
   const int h = blockIdx.y, b = blockIdx.z;
   const int C = H * D;
@@ -341,17 +341,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
 
   const int t_begin = k0 / 64;
   const int t_end = (T + 63) / 64;
-  DualTile<D> stQ, stdO;
+  RowTile<D> stQ, stdO;
   auto stage_load = [&](int t) {
     const int qt0 = t * 64;
     stQ.load(rQ, ld, qt0, T);
     stdO.load(rO, C, qt0, T);
   };
   auto stage_store = [&](int t, int buf) {
-    stQ.store_row(sQ[buf]);
-    stQ.store_tr(sQt[buf]);
-    stdO.store_row(sdO[buf]);
-    stdO.store_tr(sdOt[buf]);
+    stQ.store(sQ[buf]);
+    stdO.store(sdO[buf]);
     const int qt0 = t * 64;
     if (threadIdx.x < 64) {
       const int q = qt0 + threadIdx.x;
@@ -370,52 +368,83 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
     const int qt0 = t * 64;
     if (more) stage_load(t + 1);
     if (qt0 + 63 >= kw && kw < T) {
+      // S = Q K^T and dP = dO V^T for two 32-query sub-tiles (4 accumulators);
+      // step s+1 fragments are read while step s runs
       f32x16 S[2], dP[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { S[it][r] = 0.0f; dP[it][r] = 0.0f; }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          S[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sQ[cur], 32 * it + li, s, hf), kf[s], S[it],
-                                                          0, 0, 0);
-          dP[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sdO[cur], 32 * it + li, s, hf), vf[s],
-                                                           dP[it], 0, 0, 0);
-        }
-      }
-      float p[2][16], ds[2][16];
-      const bool need_mask = (qt0 < kw + 31) || (qt0 + 64 > T) || (kw + 32 > T);
 #pragma unroll
       for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int il = 32 * it + 8 * g + 4 * hf;
-          const float4 L4 = *reinterpret_cast<const float4*>(&sL[cur][il]);
-          const float4 D4 = *reinterpret_cast<const float4*>(&sDl[cur][il]);
-          const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
-          const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+        for (int r = 0; r < 16; ++r) { S[it][r] = 0.0f; dP[it][r] = 0.0f; }
+      bf16x8 qfr[2][2], ofr[2][2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float pv = exp2f(fmaf(S[it][r], scale_log2, -Ls[e]));
-            if (need_mask) {
-              const int qi = qt0 + il + e;
-              if (qi < kj || qi >= T || kj >= T) pv = 0.0f;
-            }
-            p[it][r] = pv;
-            ds[it][r] = pv * (dP[it][r] - Ds[e]);
+      for (int it = 0; it < 2; ++it) {
+        qfr[0][it] = row_frag<D>(sQ[cur], 32 * it + li, 0, hf);
+        ofr[0][it] = row_frag<D>(sdO[cur], 32 * it + li, 0, hf);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            qfr[(s + 1) & 1][it] = row_frag<D>(sQ[cur], 32 * it + li, s + 1, hf);
+            ofr[(s + 1) & 1][it] = row_frag<D>(sdO[cur], 32 * it + li, s + 1, hf);
           }
         }
 #pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          S[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[s & 1][it], kf[s], S[it], 0, 0, 0);
+          dP[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ofr[s & 1][it], vf[s], dP[it], 0, 0, 0);
+        }
+      }
+      float p[2][16], ds[2][16];
+      auto probs = [&](auto masked) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int il = 32 * it + 8 * g + 4 * hf;
+            const float4 L4 = *reinterpret_cast<const float4*>(&sL[cur][il]);
+            const float4 D4 = *reinterpret_cast<const float4*>(&sDl[cur][il]);
+            const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pv = __builtin_amdgcn_exp2f(fmaf(S[it][r], scale_log2, -Ls[e]));
+              if constexpr (decltype(masked)::value) {
+                const int qi = qt0 + il + e;
+                if (qi < kj || qi >= T || kj >= T) pv = 0.0f;
+              }
+              p[it][r] = pv;
+              ds[it][r] = pv * (dP[it][r] - Ds[e]);
+            }
+          }
+      };
+      if ((qt0 < kw + 31) || (qt0 + 64 > T) || (kw + 32 > T)) probs(std::true_type{});
+      else probs(std::false_type{});
+      // dV^T += dO^T P and dK^T += Q^T dS; transposed fragments of step
+      // ks+1 are read while step ks runs
+      bf16x8 tor[2][DT], tqr[2][DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        tor[0][dt] = tr_frag<D>(sdO[cur], dt, 0, lane);
+        tqr[0][dt] = tr_frag<D>(sQ[cur], dt, 0, lane);
+      }
+#pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            tor[(ks + 1) & 1][dt] = tr_frag<D>(sdO[cur], dt, ks + 1, lane);
+            tqr[(ks + 1) & 1][dt] = tr_frag<D>(sQ[cur], dt, ks + 1, lane);
+          }
+        }
         const bf16x8 pb = pack_slots(p[ks >> 1], 2 * (ks & 1));
         const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sdOt[cur], 32 * dt + li, ks, hf), pb, dv[dt], 0,
-                                                           0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sQt[cur], 32 * dt + li, ks, hf), db, dk[dt], 0,
-                                                           0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tor[ks & 1][dt], pb, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tqr[ks & 1][dt], db, dk[dt], 0, 0, 0);
         }
       }
     }
@@ -443,7 +472,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
 
 // ---------------------------------------------------------- backward dQ (MFMA)
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                            const bf16* __restrict__ dO,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ delta,
@@ -452,7 +481,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
-  __shared__ uint2 sKt[2][D * 16];
   const int nqb = (T + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -489,12 +517,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  DualTile<D> stK;
-  RowTile<D> stV;
+  RowTile<D> stK, stV;
   stK.load(rK, ld, 0, T);
   stV.load(rV, ld, 0, T);
-  stK.store_row(sK[0]);
-  stK.store_tr(sKt[0]);
+  stK.store(sK[0]);
   stV.store(sV[0]);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
@@ -506,44 +532,68 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
       stV.load(rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
+      // S^T = K Q^T and dP^T = V dO^T for two 32-key sub-tiles (4
+      // accumulators); step s+1 fragments are read while step s runs
       f32x16 St[2], dPt[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { St[jt][r] = 0.0f; dPt[jt][r] = 0.0f; }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          St[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sK[cur], 32 * jt + li, s, hf), qf[s], St[jt],
-                                                           0, 0, 0);
-          dPt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sV[cur], 32 * jt + li, s, hf), df[s],
-                                                            dPt[jt], 0, 0, 0);
-        }
-      }
-      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T) || (qw + 32 > T);
-      float ds[2][16];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2f(fmaf(St[jt][r], scale_log2, -L2));
-          if (need_mask) {
-            const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (j > qi || j >= T || qi >= T) pv = 0.0f;
+        for (int r = 0; r < 16; ++r) { St[jt][r] = 0.0f; dPt[jt][r] = 0.0f; }
+      bf16x8 kfr[2][2], vfr[2][2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        kfr[0][jt] = row_frag<D>(sK[cur], 32 * jt + li, 0, hf);
+        vfr[0][jt] = row_frag<D>(sV[cur], 32 * jt + li, 0, hf);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            kfr[(s + 1) & 1][jt] = row_frag<D>(sK[cur], 32 * jt + li, s + 1, hf);
+            vfr[(s + 1) & 1][jt] = row_frag<D>(sV[cur], 32 * jt + li, s + 1, hf);
           }
-          ds[jt][r] = pv * (dPt[jt][r] - Dl);
         }
 #pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          St[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s & 1][jt], qf[s], St[jt], 0, 0, 0);
+          dPt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[s & 1][jt], df[s], dPt[jt], 0, 0, 0);
+        }
+      }
+      float ds[2][16];
+      auto grads = [&](auto masked) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = __builtin_amdgcn_exp2f(fmaf(St[jt][r], scale_log2, -L2));
+            if constexpr (decltype(masked)::value) {
+              const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (j > qi || j >= T || qi >= T) pv = 0.0f;
+            }
+            ds[jt][r] = pv * (dPt[jt][r] - Dl);
+          }
+      };
+      if ((kv0 + 63 > qw) || (kv0 + 64 > T) || (qw + 32 > T)) grads(std::true_type{});
+      else grads(std::false_type{});
+      // dQ^T += K^T dS^T; K^T fragments of step ks+1 are read during step ks
+      bf16x8 tkr[2][DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) tkr[0][dt] = tr_frag<D>(sK[cur], dt, 0, lane);
+#pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) tkr[(ks + 1) & 1][dt] = tr_frag<D>(sK[cur], dt, ks + 1, lane);
+        }
         const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sKt[cur], 32 * dt + li, ks, hf), db, dq[dt], 0, 0,
-                                                           0);
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkr[ks & 1][dt], db, dq[dt], 0, 0, 0);
       }
     }
     if (more) {
-      stK.store_row(sK[cur ^ 1]);
-      stK.store_tr(sKt[cur ^ 1]);
+      stK.store(sK[cur ^ 1]);
       stV.store(sV[cur ^ 1]);
     }
     __syncthreads();

@@ -157,9 +157,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Operand with k contiguous in HBM: R rows x 64 k, thread t covers unit
-// c = t & 7 of rows (t >> 3) + 32 i.
+// LDS swizzles (16-byte units, XOR by row) chosen so that the fragment
+// reads below are free of bank conflicts on a 64-bank LDS:
+//   k-contiguous tiles, 128-byte rows: f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+//   k-major tiles, 256/512-byte rows:   f(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+__device__ __forceinline__ int swz128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swzq(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Operand with k contiguous in HBM: R rows x 64 k, LDS [row][8 units];
+// thread t covers unit c = t & 7 of rows (t >> 3) + 32 i.
 template <int R>
 struct StageKc {
   static constexpr int NV = R / 32;
@@ -181,57 +189,57 @@ struct StageKc {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int row = (t >> 3) + 32 * i;
-      lds[row * 8 + (c ^ (row & 7))] = v[i];
+      lds[row * 8 + (c ^ swz128(row))] = v[i];
     }
+  }
+  // A/B operand fragment: tile row `row`, k-step kk, lane half hf
+  static __device__ __forceinline__ bf16x8 frag(const uint4* lds, int row, int kk, int lane) {
+    return __builtin_bit_cast(bf16x8, lds[row * 8 + ((2 * kk + (lane >> 5)) ^ swz128(row))]);
   }
 };
 
-// Operand with rows contiguous in HBM ([K][ld]): 8 x 8 sub-blocks
-// s = t + 256 i, kg = s & 7 (k rows 8kg..8kg+7), rg = s >> 3 (rows 8rg..).
+// Operand with rows contiguous in HBM ([K][ld]): staged as-is, LDS
+// [64 k][R / 8 units], and read transposed with ds_read_b64_tr_b16: within a
+// 16-lane group, lane i receives element i % 4 of the 4-element vectors
+// addressed by lanes 4 q + i / 4 (q = 0..3).
 template <int R>
 struct StageKm {
-  static constexpr int NS = (R + 255) / 256;
-  uint4 v[NS][8];
+  static constexpr int UPR = R / 8;
+  static constexpr int NV = 64 * UPR / 256;
+  uint4 v[NV];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax, int k0, int kend) {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int s = t + 256 * i;
-      const int kg = s & 7, rg = s >> 3;
-      const int gr = r0 + 8 * rg;
-      const bool rok = s < R && gr + 8 <= rmax;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + 8 * kg + j;
-        const uint32_t off = (rok && gk < kend) ? (uint32_t)(((long)gk * ld + gr) * 2) : OOB;
-        v[i][j] = bload(rs, off);
-      }
+    for (int i = 0; i < NV; ++i) {
+      const int u = t + 256 * i;
+      const int kr = u / UPR, c = u % UPR;
+      const int gk = k0 + kr, gc = r0 + 8 * c;
+      const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
+      v[i] = bload(rs, off);
     }
   }
   __device__ __forceinline__ void store(uint4* lds) const {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int s = t + 256 * i;
-      if (s >= R) continue;
-      const int kg = s & 7, rg = s >> 3;
-      const uint32_t* w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = reinterpret_cast<const uint32_t*>(&v[i][j]);
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        // element rr of each k-row j, packed in k order
-        const int word = rr >> 1;
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t lo = w[2 * q][word], hi = w[2 * q + 1][word];
-          o[q] = (rr & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        const int row = 8 * rg + rr;
-        lds[row * 8 + (kg ^ rr)] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+    for (int i = 0; i < NV; ++i) {
+      const int u = t + 256 * i;
+      const int kr = u / UPR, c = u % UPR;
+      lds[kr * UPR + (c ^ swzq(kr))] = v[i];
     }
+  }
+  static __device__ __forceinline__ i16x4 tr(const uint4* lds, int krow, int col) {
+    const bf16* base = reinterpret_cast<const bf16*>(lds);
+    const int off = (krow * UPR + ((col >> 3) ^ swzq(krow))) * 8 + (col & 7);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + off));
+  }
+  // fragment of tile column `row` (an m or n index): k slots 16 kk + 8 hf + 0..7
+  static __device__ __forceinline__ bf16x8 frag(const uint4* lds, int row, int kk, int lane) {
+    const int i = lane & 15;
+    const int col = (row & ~15) + 4 * (i & 3);
+    const int k0 = 16 * kk + 8 * (lane >> 5) + (i >> 2);
+    const i16x4 a = tr(lds, k0, col);
+    const i16x4 b = tr(lds, k0 + 4, col);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 
@@ -296,20 +304,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
     const uint4* As = lds + cur * STAGE_UNITS;
     const uint4* Bs = As + BM * 8;
     // fragments of k-step kk+1 are read while the MFMAs of step kk run
+    using SA = Stage<A_KMAJ, BM>;
+    using SB = Stage<B_KMAJ, BN>;
     bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = as_bf16x8(As[(wm + 32 * i + lrow) * 8 + (lhalf ^ (lrow & 7))]);
+    for (int i = 0; i < TM; ++i) af[0][i] = SA::frag(As, wm + 32 * i + lrow, 0, lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = as_bf16x8(Bs[(wn + 32 * j + lrow) * 8 + (lhalf ^ (lrow & 7))]);
+    for (int j = 0; j < TN; ++j) bfr[0][j] = SB::frag(Bs, wn + 32 * j + lrow, 0, lane);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int cb = kk & 1;
       if (kk + 1 < BK / 16) {
-        const int unit = (2 * (kk + 1) + lhalf) ^ (lrow & 7);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[cb ^ 1][i] = as_bf16x8(As[(wm + 32 * i + lrow) * 8 + unit]);
+        for (int i = 0; i < TM; ++i) af[cb ^ 1][i] = SA::frag(As, wm + 32 * i + lrow, kk + 1, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[cb ^ 1][j] = as_bf16x8(Bs[(wn + 32 * j + lrow) * 8 + unit]);
+        for (int j = 0; j < TN; ++j) bfr[cb ^ 1][j] = SB::frag(Bs, wn + 32 * j + lrow, kk + 1, lane);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -317,6 +326,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
         for (int i = 0; i < TM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
     }
+    // the next tile's LDS stores stay after this tile's fragment reads
+    asm volatile("" ::: "memory");
     if (more) {
       uint4* nxt = lds + (cur ^ 1) * STAGE_UNITS;
       sa.store(nxt);
@@ -457,10 +468,14 @@ Plan plan_mfma(const GemmDesc& d) {
   if (d.epi == EPI_XENT_STATS || t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else { pl.BMv = 128; pl.BNv = 128; }
   const long tiles = (long)cdiv(d.M, pl.BMv) * cdiv(d.N, pl.BNv);
+  // split until the blocks cover the 256 CUs once (each split adds an fp32
+  // partial of the whole output to write and reduce)
+  const long slots = 256;
   pl.splits = 1;
   if (d.epi == EPI_F32) {
-    // weight gradients: small output, long K -> split K to fill 256 CUs
-    while (tiles * pl.splits < 200 && d.K / (pl.splits * 2) >= 512) pl.splits *= 2;
+    // weight gradients: small output, long K -> split K (fp32 partials,
+    // fixed-order reduce) until every CU has work
+    while (tiles * pl.splits < slots && d.K / (pl.splits * 2) >= 256) pl.splits *= 2;
   }
   pl.k_split = cdiv(cdiv(d.K, pl.splits), BK) * BK;
   pl.splits = cdiv(d.K, pl.k_split);
