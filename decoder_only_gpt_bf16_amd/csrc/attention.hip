@@ -110,7 +110,27 @@ struct RowTile {
       s[upos<D>(u / KU, u % KU)] = v[i];
     }
   }
+  // Asynchronous global -> LDS copy of rows r0 .. r0 + 63 (no registers):
+  // wave w's instruction i fills physical units P = (4 i + w) * 64 + lane,
+  // i.e. row P / KU, slot P % KU, which holds logical unit slot ^ f(row);
+  // lane L's 16 bytes land at the wave-uniform base + 16 L, and rows >= T
+  // (out-of-range offsets) arrive as zeros.
+  static __device__ __forceinline__ void direct(uint4* s, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int row = P / KU;
+      const int u = (P % KU) ^ swz<D>(row);
+      const int r = r0 + row;
+      const uint32_t off = r < T ? (uint32_t)(((long)r * ld + 8 * u) * 2) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(s + (4 * i + w) * 64),
+                                               16, off, 0, 0, 0);
+    }
+  }
 };
+
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // A operand from tile rows: row r, k-step ks (columns 16 ks + 8 hf .. + 7).
 template <int D>
@@ -177,11 +197,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D> stK, stV;
-  stK.load(rK, ld, 0, T);
-  stV.load(rV, ld, 0, T);
-  stK.store(sK[0]);
-  stV.store(sV[0]);
+  RowTile<D>::direct(sK[0], rK, ld, 0, T);
+  RowTile<D>::direct(sV[0], rV, ld, 0, T);
+  wait_lds_loads();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -189,8 +207,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
-      stK.load(rK, ld, kv0 + 64, T);
-      stV.load(rV, ld, kv0 + 64, T);
+      RowTile<D>::direct(sK[cur ^ 1], rK, ld, kv0 + 64, T);
+      RowTile<D>::direct(sV[cur ^ 1], rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
       // S^T = K Q^T for two 32-key sub-tiles; k-step s+1 fragments are read
@@ -271,10 +289,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ks & 1][dt], pb, acc[dt], 0, 0, 0);
       }
     }
-    if (more) {
-      stK.store(sK[cur ^ 1]);
-      stV.store(sV[cur ^ 1]);
-    }
+    wait_lds_loads();
     __syncthreads();
   }
 
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
 
 // ------------------------------------------------------ backward dK, dV (MFMA)
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                              const bf16* __restrict__ dO,
                                                              const float* __restrict__ lse,
                                                              const float* __restrict__ delta,
@@ -341,65 +356,56 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
 
   const int t_begin = k0 / 64;
   const int t_end = (T + 63) / 64;
-  RowTile<D> stQ, stdO;
-  auto stage_load = [&](int t) {
+  // Q and dO tiles stream global -> LDS asynchronously; the tile's log-sum-exp
+  // and delta values are prefetched into registers one tile ahead
+  float lpre = 0.0f, dpre = 0.0f;
+  auto stage_issue = [&](int t, int buf) {
     const int qt0 = t * 64;
-    stQ.load(rQ, ld, qt0, T);
-    stdO.load(rO, C, qt0, T);
-  };
-  auto stage_store = [&](int t, int buf) {
-    stQ.store(sQ[buf]);
-    stdO.store(sdO[buf]);
-    const int qt0 = t * 64;
+    RowTile<D>::direct(sQ[buf], rQ, ld, qt0, T);
+    RowTile<D>::direct(sdO[buf], rO, C, qt0, T);
     if (threadIdx.x < 64) {
       const int q = qt0 + threadIdx.x;
-      sL[buf][threadIdx.x] = q < T ? Lg[q] * LOG2E : 0.0f;
-      sDl[buf][threadIdx.x] = q < T ? Dg[q] : 0.0f;
+      lpre = q < T ? Lg[q] * LOG2E : 0.0f;
+      dpre = q < T ? Dg[q] : 0.0f;
     }
   };
+  auto stage_finish = [&](int buf) {
+    if (threadIdx.x < 64) {
+      sL[buf][threadIdx.x] = lpre;
+      sDl[buf][threadIdx.x] = dpre;
+    }
+    wait_lds_loads();
+  };
   if (t_begin < t_end) {
-    stage_load(t_begin);
-    stage_store(t_begin, 0);
+    stage_issue(t_begin, 0);
+    stage_finish(0);
   }
   __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
     const int cur = (t - t_begin) & 1;
     const bool more = t + 1 < t_end;
     const int qt0 = t * 64;
-    if (more) stage_load(t + 1);
+    if (more) stage_issue(t + 1, cur ^ 1);
     if (qt0 + 63 >= kw && kw < T) {
-      // S = Q K^T and dP = dO V^T for two 32-query sub-tiles (4 accumulators);
-      // step s+1 fragments are read while step s runs
-      f32x16 S[2], dP[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { S[it][r] = 0.0f; dP[it][r] = 0.0f; }
-      bf16x8 qfr[2][2], ofr[2][2];
+      // the 64-query tile is processed as two 32-query halves: S = Q K^T and
+      // dP = dO V^T for the half, P and dS, then dV^T += dO^T P and
+      // dK^T += Q^T dS over it; only one half's scores are live at a time
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
-        qfr[0][it] = row_frag<D>(sQ[cur], 32 * it + li, 0, hf);
-        ofr[0][it] = row_frag<D>(sdO[cur], 32 * it + li, 0, hf);
-      }
+        const int q0h = qt0 + 32 * it;
+        if (q0h + 31 < kw) continue;  // every query of this half precedes the wave's keys
+        f32x16 S, dP;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) {
+        for (int r = 0; r < 16; ++r) { S[r] = 0.0f; dP[r] = 0.0f; }
 #pragma unroll
-          for (int it = 0; it < 2; ++it) {
-            qfr[(s + 1) & 1][it] = row_frag<D>(sQ[cur], 32 * it + li, s + 1, hf);
-            ofr[(s + 1) & 1][it] = row_frag<D>(sdO[cur], 32 * it + li, s + 1, hf);
-          }
+        for (int s = 0; s < KS; ++s) {
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sQ[cur], 32 * it + li, s, hf), kf[s], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sdO[cur], 32 * it + li, s, hf), vf[s], dP, 0, 0, 0);
         }
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          S[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[s & 1][it], kf[s], S[it], 0, 0, 0);
-          dP[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ofr[s & 1][it], vf[s], dP[it], 0, 0, 0);
-        }
-      }
-      float p[2][16], ds[2][16];
-      auto probs = [&](auto masked) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
+        // P and dS go straight to packed bf16 B operands (k-slot order of
+        // pack_slots: registers 8 kh + 0..7)
+        uint32_t pw[8], dw[8];
+        auto probs = [&](auto masked) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int il = 32 * it + 8 * g + 4 * hf;
@@ -407,48 +413,41 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
             const float4 D4 = *reinterpret_cast<const float4*>(&sDl[cur][il]);
             const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
             const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+            float pv[4], dv4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
-              float pv = __builtin_amdgcn_exp2f(fmaf(S[it][r], scale_log2, -Ls[e]));
+              float x = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, -Ls[e]));
               if constexpr (decltype(masked)::value) {
                 const int qi = qt0 + il + e;
-                if (qi < kj || qi >= T || kj >= T) pv = 0.0f;
+                if (qi < kj || qi >= T || kj >= T) x = 0.0f;
               }
-              p[it][r] = pv;
-              ds[it][r] = pv * (dP[it][r] - Ds[e]);
+              pv[e] = x;
+              dv4[e] = x * (dP[r] - Ds[e]);
             }
+            pw[2 * g] = pack2(pv[0], pv[1]);
+            pw[2 * g + 1] = pack2(pv[2], pv[3]);
+            dw[2 * g] = pack2(dv4[0], dv4[1]);
+            dw[2 * g + 1] = pack2(dv4[2], dv4[3]);
           }
-      };
-      if ((qt0 < kw + 31) || (qt0 + 64 > T) || (kw + 32 > T)) probs(std::true_type{});
-      else probs(std::false_type{});
-      // dV^T += dO^T P and dK^T += Q^T dS; transposed fragments of step
-      // ks+1 are read while step ks runs
-      bf16x8 tor[2][DT], tqr[2][DT];
+        };
+        if ((q0h < kw + 31) || (q0h + 32 > T) || (kw + 32 > T)) probs(std::true_type{});
+        else probs(std::false_type{});
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        tor[0][dt] = tr_frag<D>(sdO[cur], dt, 0, lane);
-        tqr[0][dt] = tr_frag<D>(sQ[cur], dt, 0, lane);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
+        for (int kh = 0; kh < 2; ++kh) {
+          const bf16x8 pb = u4_bf8(make_uint4(pw[4 * kh], pw[4 * kh + 1], pw[4 * kh + 2], pw[4 * kh + 3]));
+          const bf16x8 db = u4_bf8(make_uint4(dw[4 * kh], dw[4 * kh + 1], dw[4 * kh + 2], dw[4 * kh + 3]));
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            tor[(ks + 1) & 1][dt] = tr_frag<D>(sdO[cur], dt, ks + 1, lane);
-            tqr[(ks + 1) & 1][dt] = tr_frag<D>(sQ[cur], dt, ks + 1, lane);
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sdO[cur], dt, 2 * it + kh, lane), pb, dv[dt],
+                                                             0, 0, 0);
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sQ[cur], dt, 2 * it + kh, lane), db, dk[dt],
+                                                             0, 0, 0);
           }
-        }
-        const bf16x8 pb = pack_slots(p[ks >> 1], 2 * (ks & 1));
-        const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tor[ks & 1][dt], pb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tqr[ks & 1][dt], db, dk[dt], 0, 0, 0);
         }
       }
     }
-    if (more) stage_store(t + 1, cur ^ 1);
+    if (more) stage_finish(cur ^ 1);
     __syncthreads();
   }
   if (kj < T) {
@@ -472,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(int T, int H, const
 
 // ---------------------------------------------------------- backward dQ (MFMA)
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                            const bf16* __restrict__ dO,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ delta,
@@ -517,85 +516,60 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(int T, int H, const b
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D> stK, stV;
-  stK.load(rK, ld, 0, T);
-  stV.load(rV, ld, 0, T);
-  stK.store(sK[0]);
-  stV.store(sV[0]);
+  RowTile<D>::direct(sK[0], rK, ld, 0, T);
+  RowTile<D>::direct(sV[0], rV, ld, 0, T);
+  wait_lds_loads();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
-      stK.load(rK, ld, kv0 + 64, T);
-      stV.load(rV, ld, kv0 + 64, T);
+      RowTile<D>::direct(sK[cur ^ 1], rK, ld, kv0 + 64, T);
+      RowTile<D>::direct(sV[cur ^ 1], rV, ld, kv0 + 64, T);
     }
     if (kv0 <= qw + 31 && qw < T) {
-      // S^T = K Q^T and dP^T = V dO^T for two 32-key sub-tiles (4
-      // accumulators); step s+1 fragments are read while step s runs
-      f32x16 St[2], dPt[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { St[jt][r] = 0.0f; dPt[jt][r] = 0.0f; }
-      bf16x8 kfr[2][2], vfr[2][2];
+      // the 64-key tile is processed as two 32-key halves: S^T = K Q^T and
+      // dP^T = V dO^T for the half, dS^T, then dQ^T += K^T dS^T over it;
+      // only one half's scores are live at a time
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        kfr[0][jt] = row_frag<D>(sK[cur], 32 * jt + li, 0, hf);
-        vfr[0][jt] = row_frag<D>(sV[cur], 32 * jt + li, 0, hf);
-      }
+        if (kv0 + 32 * jt > qw + 31) break;  // half above the diagonal
+        f32x16 St, dPt;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) {
+        for (int r = 0; r < 16; ++r) { St[r] = 0.0f; dPt[r] = 0.0f; }
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            kfr[(s + 1) & 1][jt] = row_frag<D>(sK[cur], 32 * jt + li, s + 1, hf);
-            vfr[(s + 1) & 1][jt] = row_frag<D>(sV[cur], 32 * jt + li, s + 1, hf);
-          }
+        for (int s = 0; s < KS; ++s) {
+          St = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sK[cur], 32 * jt + li, s, hf), qf[s], St, 0, 0, 0);
+          dPt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sV[cur], 32 * jt + li, s, hf), df[s], dPt, 0, 0,
+                                                        0);
         }
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          St[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s & 1][jt], qf[s], St[jt], 0, 0, 0);
-          dPt[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[s & 1][jt], df[s], dPt[jt], 0, 0, 0);
-        }
-      }
-      float ds[2][16];
-      auto grads = [&](auto masked) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        float ds[16];
+        auto grads = [&](auto masked) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(fmaf(St[jt][r], scale_log2, -L2));
+            float pv = __builtin_amdgcn_exp2f(fmaf(St[r], scale_log2, -L2));
             if constexpr (decltype(masked)::value) {
               const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
               if (j > qi || j >= T || qi >= T) pv = 0.0f;
             }
-            ds[jt][r] = pv * (dPt[jt][r] - Dl);
+            ds[r] = pv * (dPt[r] - Dl);
           }
-      };
-      if ((kv0 + 63 > qw) || (kv0 + 64 > T) || (qw + 32 > T)) grads(std::true_type{});
-      else grads(std::false_type{});
-      // dQ^T += K^T dS^T; K^T fragments of step ks+1 are read during step ks
-      bf16x8 tkr[2][DT];
+        };
+        const int k0 = kv0 + 32 * jt;
+        if ((k0 + 31 > qw) || (k0 + 32 > T) || (qw + 32 > T)) grads(std::true_type{});
+        else grads(std::false_type{});
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) tkr[0][dt] = tr_frag<D>(sK[cur], dt, 0, lane);
+        for (int kh = 0; kh < 2; ++kh) {
+          const bf16x8 db = pack_slots(ds, 2 * kh);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) tkr[(ks + 1) & 1][dt] = tr_frag<D>(sK[cur], dt, ks + 1, lane);
+          for (int dt = 0; dt < DT; ++dt)
+            dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sK[cur], dt, 2 * jt + kh, lane), db, dq[dt],
+                                                             0, 0, 0);
         }
-        const bf16x8 db = pack_slots(ds[ks >> 1], 2 * (ks & 1));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tkr[ks & 1][dt], db, dq[dt], 0, 0, 0);
       }
     }
-    if (more) {
-      stK.store(sK[cur ^ 1]);
-      stV.store(sV[cur ^ 1]);
-    }
+    wait_lds_loads();
     __syncthreads();
   }
   if (qi < T) {

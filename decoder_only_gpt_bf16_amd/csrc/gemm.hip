@@ -166,6 +166,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swzq(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// Asynchronous global -> LDS copy of 16 bytes per lane: lane L's vector
+// lands at LDS byte address lds_base + 16 L (lds_base wave-uniform); an
+// out-of-range offset writes zeros.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Operand with k contiguous in HBM: R rows x 64 k, LDS [row][8 units];
 // thread t covers unit c = t & 7 of rows (t >> 3) + 32 i.
 template <int R>
@@ -190,6 +198,22 @@ struct StageKc {
     for (int i = 0; i < NV; ++i) {
       const int row = (t >> 3) + 32 * i;
       lds[row * 8 + (c ^ swz128(row))] = v[i];
+    }
+  }
+  // Direct copy: wave w's instruction i fills physical units
+  // P = (4 i + w) * 64 + lane, i.e. row P / 8, slot P % 8, which holds
+  // logical unit (P % 8) ^ f(row).
+  static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                int k0, int kend) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < R / 32; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int row = P >> 3;
+      const int u = (P & 7) ^ swz128(row);
+      const int gr = r0 + row, kk = k0 + 8 * u;
+      const uint32_t off = (kk + 8 <= kend && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
+      load_lds16(rs, lds + (4 * i + w) * 64, off);
     }
   }
   // A/B operand fragment: tile row `row`, k-step kk, lane half hf
@@ -225,6 +249,21 @@ struct StageKm {
       const int u = t + 256 * i;
       const int kr = u / UPR, c = u % UPR;
       lds[kr * UPR + (c ^ swzq(kr))] = v[i];
+    }
+  }
+  // Direct copy: physical unit P = (4 i + w) * 64 + lane is k-row P / UPR,
+  // slot P % UPR, holding logical unit (P % UPR) ^ f(k-row).
+  static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                int k0, int kend) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int P = (4 * i + w) * 64 + lane;
+      const int kr = P / UPR;
+      const int c = (P % UPR) ^ swzq(kr);
+      const int gk = k0 + kr, gc = r0 + 8 * c;
+      const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
+      load_lds16(rs, lds + (4 * i + w) * 64, off);
     }
   }
   static __device__ __forceinline__ i16x4 tr(const uint4* lds, int krow, int col) {
@@ -281,31 +320,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  Stage<A_KMAJ, BM> sa;
-  Stage<B_KMAJ, BN> sb;
+  using SA = Stage<A_KMAJ, BM>;
+  using SB = Stage<B_KMAJ, BN>;
+  // tiles are copied global -> LDS asynchronously (no staging registers):
+  // tile kt+1 streams into the other buffer while tile kt is multiplied
   if (nk > 0) {
-    sa.load(ra, p.lda, m0, p.M, kbeg, kend);
-    sb.load(rb, p.ldb, n0, p.N, kbeg, kend);
-    sa.store(lds);
-    sb.store(lds + BM * 8);
+    SA::direct(lds, ra, p.lda, m0, p.M, kbeg, kend);
+    SB::direct(lds + BM * 8, rb, p.ldb, n0, p.N, kbeg, kend);
   }
+  wait_lds_loads();
   __syncthreads();
 
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
+    if (kt + 1 < nk) {
       const int k0 = kbeg + (kt + 1) * BK;
-      sa.load(ra, p.lda, m0, p.M, k0, kend);
-      sb.load(rb, p.ldb, n0, p.N, k0, kend);
+      uint4* nxt = lds + (cur ^ 1) * STAGE_UNITS;
+      SA::direct(nxt, ra, p.lda, m0, p.M, k0, kend);
+      SB::direct(nxt + BM * 8, rb, p.ldb, n0, p.N, k0, kend);
     }
     const uint4* As = lds + cur * STAGE_UNITS;
     const uint4* Bs = As + BM * 8;
     // fragments of k-step kk+1 are read while the MFMAs of step kk run
-    using SA = Stage<A_KMAJ, BM>;
-    using SB = Stage<B_KMAJ, BN>;
     bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[0][i] = SA::frag(As, wm + 32 * i + lrow, 0, lane);
@@ -326,13 +364,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
         for (int i = 0; i < TM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
     }
-    // the next tile's LDS stores stay after this tile's fragment reads
-    asm volatile("" ::: "memory");
-    if (more) {
-      uint4* nxt = lds + (cur ^ 1) * STAGE_UNITS;
-      sa.store(nxt);
-      sb.store(nxt + BM * 8);
-    }
+    wait_lds_loads();
     __syncthreads();
   }
 
