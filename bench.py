@@ -22,6 +22,21 @@ import time
 METRIC = "train tokens/s (fwd+bwd) on 1 GPU, d20 shape; % bf16 MFMA peak"
 PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "hbm_traffic_d20_block_fwd_bwd.md")
+CSRC = os.path.join(HERE, "decoder_only_gpt_bf16_amd", "csrc")
+
+# call site -> (kernel as named in the counter summary, its source files);
+# sites that share a GEMM instance with others have no entry
+SITE_KERNEL = {
+    "attn_fwd": ("attn_fwd_mfma<128>", "attention"), "attn_bwd_dkdv": ("attn_bwd_dkdv_mfma<128>", "attention"),
+    "attn_bwd_dq": ("attn_bwd_dq_mfma<128>", "attention"), "qk_rope_norm": ("qk_fwd_k<...>", "attention"),
+    "qk_bwd": ("qk_bwd_k<...>", "attention"), "attn_delta": ("delta_k<...>", "attention"),
+    "qkv_gemm": ("gemm_mfma<false, false, 0, 256, 256>", "gemm"),
+    "fc_gemm_gelu": ("gemm_mfma<false, false, 1, 256, 256>", "gemm"),
+    "proj_dgrad_gelu": ("gemm_mfma<false, true, 2, 256, 256>", "gemm"),
+}
+SOURCES = {"attention": ["attention.hip", "common.h", "kernels.h"], "gemm": ["gemm.hip", "common.h", "kernels.h"]}
 
 
 def block_flops(B, T, C, H):
@@ -60,8 +75,36 @@ def site_work(name, B, T, C, H):
     return None, None
 
 
-def cpu_baseline(w, budget_s=30.0):
-    """The float64 oracle on one sequence of the workload (B=1 of 4)."""
+def source_hash(family):
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(site):
+    """HBM bytes per launch of a call site's kernel (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated) from the committed counter summary, or None when the
+    site's kernel is not uniquely named there or its sources changed since
+    the counters were taken."""
+    if site not in SITE_KERNEL or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    kernel, fam = SITE_KERNEL[site]
+    want = source_hash(fam)
+    with open(TRAFFIC_PROFILE) as fh:
+        for line in fh:
+            cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and cells[0] == kernel:
+                return int(cells[4]) if cells[5] == want else None
+    return None
+
+
+def cpu_baseline(w, min_s=12.0):
+    """The float64 oracle on whole sequences of the workload, one at a time
+    (sequence b of the same seeded batch), until at least min_s seconds of CPU
+    work have run."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -70,15 +113,18 @@ def cpu_baseline(w, budget_s=30.0):
         cores = len(os.sched_getaffinity(0))
     import oracle as O
     from decoder_only_gpt_bf16_amd import synth
-    ws = synth.scaled(w, B=1)
-    x, dy, p = synth.make_block_inputs(ws)
-    cfg = synth.oracle_cfg(ws.cfg)
+    x, dy, p = synth.make_block_inputs(w)
+    cfg = synth.oracle_cfg(w.cfg)
+    n, dt = 0, 0.0
     t0 = time.perf_counter()
-    y, cache = O.block_fwd(cfg, x, p)
-    O.block_bwd(cfg, dy, cache, p)
-    dt = time.perf_counter() - t0
-    return {"value": ws.B * ws.T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one sequence (B=1, T={ws.T}) of the d20 block fwd+bwd in float64 NumPy, {dt:.1f} s"}
+    while dt < min_s:
+        b = n % w.B
+        y, cache = O.block_fwd(cfg, x[b:b + 1], p)
+        O.block_bwd(cfg, dy[b:b + 1], cache, p)
+        n += 1
+        dt = time.perf_counter() - t0
+    return {"value": n * w.T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} sequences (B=1, T={w.T} each) of the d20 block fwd+bwd in float64 NumPy, {dt:.1f} s"}
 
 
 def time_steps(fn, steps, warmup):
@@ -106,8 +152,8 @@ def main():
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (data-parallel sharding "
+              "would sit above it); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -160,7 +206,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["avg_us"] = round(us / n, 2)
     roof["work_per_launch"] = work
