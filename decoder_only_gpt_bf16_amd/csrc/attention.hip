@@ -159,6 +159,21 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint4* s, int dt, int ks, int la
 }
 
 // ------------------------------------------------------------ forward (MFMA)
+// Launch order of the causal MFMA kernels: a 1-D grid of (row blocks x H x B)
+// workgroups whose ids are dealt heaviest row block first across every
+// (batch, head) pair, so the lightest blocks form the tail of the launch.
+// With H * B a multiple of 8, all blocks of one (batch, head) land on the
+// same XCD (ids are dealt round-robin to the 8 XCDs) and share K/V in its L2.
+// rank 0 is the heaviest: the last query block (forward, dQ) or the first
+// key block (dK/dV).
+__device__ __forceinline__ void attn_block(int T, int H, int& rank, int& h, int& b) {
+  const int HB = gridDim.x / ((T + 127) / 128);
+  const int id = blockIdx.x;
+  rank = id / HB;
+  const int bh = id - rank * HB;
+  h = bh % H;
+  b = bh / H;
+}
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                         bf16* __restrict__ o, float* __restrict__ lse,
@@ -167,8 +182,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
   const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int rank, h, b;
+  attn_block(T, H, rank, h, b);
+  const int qb = nqb - 1 - rank;
   const int C = H * D;
   const long ld = 3L * C;
   const bf16* Qg = qkv + (long)b * T * ld + h * D;
@@ -322,7 +338,8 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
   __shared__ uint4 sQ[2][64 * KU];
   __shared__ uint4 sdO[2][64 * KU];
   __shared__ float sL[2][64], sDl[2][64];
-  const int h = blockIdx.y, b = blockIdx.z;
+  int rank, h, b;
+  attn_block(T, H, rank, h, b);
   const int C = H * D;
   const long ld = 3L * C;
   const bf16* Qg = qkv + (long)b * T * ld + h * D;
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
   const float* Dg = delta + ((long)b * H + h) * T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hf = lane >> 5;
-  const int k0 = blockIdx.x * 128;
+  const int k0 = rank * 128;
   const int kw = k0 + 32 * wave;
   const int kj = kw + li;
 
@@ -481,8 +498,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
   const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int rank, h, b;
+  attn_block(T, H, rank, h, b);
+  const int qb = nqb - 1 - rank;
   const int C = H * D;
   const long ld = 3L * C;
   const bf16* Qg = qkv + (long)b * T * ld + h * D;
@@ -852,7 +870,7 @@ hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qk
                            hipStream_t s) {
   if (attn_mfma_supported(dtype, D)) {
     const float scale_log2 = LOG2E / sqrtf((float)D);
-    dim3 grid(cdiv(T, 128), H, B);
+    dim3 grid(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, T, H, (const bf16*)qkv, (bf16*)o, lse, scale_log2);
     else
@@ -879,7 +897,7 @@ hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const voi
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
-    dim3 g(cdiv(T, 128), H, B);
+    dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
                          delta, (bf16*)dqkv, scale_log2, scale);
@@ -897,7 +915,7 @@ hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void*
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
-    dim3 g(cdiv(T, 128), H, B);
+    dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_bwd_dq_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
                          delta, (bf16*)dqkv, scale_log2, scale);
