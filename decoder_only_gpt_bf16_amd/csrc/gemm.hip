@@ -2,18 +2,21 @@
 // double buffering, and an fp32 SIMT kernel for fp32 storage.
 //
 // MFMA kernel layout
-//   * 256 threads = 4 wavefronts arranged 2 (M) x 2 (N); block tile BM x BN,
-//     k tile BK = 64; each wave owns (BM/2) x (BN/2) = TM x TN MFMA tiles.
-//   * Both operands live in LDS as [row][64 k] bf16 (128-byte rows, eight
-//     16-byte units); unit c of row r is stored at position c ^ (r & 7) so
-//     that the 16-byte fragment reads of 8 consecutive rows hit distinct
-//     banks.  An operand given k-major in HBM is transposed while it is
-//     staged: each thread loads an 8 (k) x 8 (row) block with eight 16-byte
-//     loads and writes eight 16-byte k-vectors.
+//   * Block tile BM x BN, k tile BK = 64, two LDS stages.  256 x 256 tiles
+//     run 8 wavefronts (2 along M x 4 along N, two per SIMD); 128 x 128
+//     tiles run 4 (2 x 2).  A wave owns TM x TN MFMA tiles of 32 x 32.
+//   * Operand tiles go global -> LDS with buffer loads that write LDS
+//     directly (no staging registers); rows and k beyond the matrix read as
+//     zeros through the buffer's range check, so the copies carry no
+//     branches.  k-contiguous operands are stored [row][64 k] (128-byte
+//     rows), k-major operands as they lie in HBM ([64 k][rows]) and are read
+//     transposed with ds_read_b64_tr_b16.  16-byte units are XOR-swizzled
+//     per row so that both read patterns are free of bank conflicts.
 //   * The MFMA is issued with the B tile as its first operand, so a lane's
 //     16 accumulators hold one output row m (lane & 31) and 4 runs of 4
-//     consecutive columns n: epilogues read bias/residual and write outputs
-//     as 4-element vectors.
+//     consecutive columns n.  The epilogue stages each 32-row strip through
+//     LDS and applies bias / residual / GELU / GELU' / cross-entropy
+//     arithmetic on 8-column row vectors.
 //   * Tiles are mapped so that blocks resident on one XCD (the hardware
 //     deals block ids round-robin over 8 XCDs) work on neighbouring tiles
 //     of a grouped order and share their operand rows in that XCD's L2.
@@ -23,7 +26,6 @@
 namespace {
 
 constexpr int BK = 64;
-constexpr int NTHREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- epilogues
@@ -174,46 +176,24 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_b
 }
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Operand with k contiguous in HBM: R rows x 64 k, LDS [row][8 units];
-// thread t covers unit c = t & 7 of rows (t >> 3) + 32 i.
-template <int R>
+// Operand with k contiguous in HBM: R rows x 64 k, LDS [row][8 units].
+// Direct copy by NT threads: wave w's instruction i fills physical units
+// P = ((NT / 64) i + w) * 64 + lane, i.e. row P / 8, slot P % 8, which holds
+// logical unit (P % 8) ^ f(row).
+template <int R, int NT>
 struct StageKc {
-  static constexpr int NV = R / 32;
-  uint4 v[NV];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax, int k0, int kend) {
-    const int t = threadIdx.x;
-    const int kk = k0 + 8 * (t & 7);
-    const bool kok = kk + 8 <= kend;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int gr = r0 + (t >> 3) + 32 * i;
-      const uint32_t off = (kok && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
-      v[i] = bload(rs, off);
-    }
-  }
-  __device__ __forceinline__ void store(uint4* lds) const {
-    const int t = threadIdx.x;
-    const int c = t & 7;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      lds[row * 8 + (c ^ swz128(row))] = v[i];
-    }
-  }
-  // Direct copy: wave w's instruction i fills physical units
-  // P = (4 i + w) * 64 + lane, i.e. row P / 8, slot P % 8, which holds
-  // logical unit (P % 8) ^ f(row).
+  static constexpr int NL = R * 8 / NT;
   static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
                                                 int k0, int kend) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
+    for (int i = 0; i < NL; ++i) {
+      const int P = (NT / 64 * i + w) * 64 + lane;
       const int row = P >> 3;
       const int u = (P & 7) ^ swz128(row);
       const int gr = r0 + row, kk = k0 + 8 * u;
       const uint32_t off = (kk + 8 <= kend && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
-      load_lds16(rs, lds + (4 * i + w) * 64, off);
+      load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
     }
   }
   // A/B operand fragment: tile row `row`, k-step kk, lane half hf
@@ -225,45 +205,23 @@ struct StageKc {
 // Operand with rows contiguous in HBM ([K][ld]): staged as-is, LDS
 // [64 k][R / 8 units], and read transposed with ds_read_b64_tr_b16: within a
 // 16-lane group, lane i receives element i % 4 of the 4-element vectors
-// addressed by lanes 4 q + i / 4 (q = 0..3).
-template <int R>
+// addressed by lanes 4 q + i / 4 (q = 0..3).  Direct copy: physical unit P is
+// k-row P / UPR, slot P % UPR, holding logical unit (P % UPR) ^ f(k-row).
+template <int R, int NT>
 struct StageKm {
   static constexpr int UPR = R / 8;
-  static constexpr int NV = 64 * UPR / 256;
-  uint4 v[NV];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax, int k0, int kend) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = t + 256 * i;
-      const int kr = u / UPR, c = u % UPR;
-      const int gk = k0 + kr, gc = r0 + 8 * c;
-      const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
-      v[i] = bload(rs, off);
-    }
-  }
-  __device__ __forceinline__ void store(uint4* lds) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = t + 256 * i;
-      const int kr = u / UPR, c = u % UPR;
-      lds[kr * UPR + (c ^ swzq(kr))] = v[i];
-    }
-  }
-  // Direct copy: physical unit P = (4 i + w) * 64 + lane is k-row P / UPR,
-  // slot P % UPR, holding logical unit (P % UPR) ^ f(k-row).
+  static constexpr int NL = 64 * UPR / NT;
   static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
                                                 int k0, int kend) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int P = (4 * i + w) * 64 + lane;
+    for (int i = 0; i < NL; ++i) {
+      const int P = (NT / 64 * i + w) * 64 + lane;
       const int kr = P / UPR;
       const int c = (P % UPR) ^ swzq(kr);
       const int gk = k0 + kr, gc = r0 + 8 * c;
       const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
-      load_lds16(rs, lds + (4 * i + w) * 64, off);
+      load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
     }
   }
   static __device__ __forceinline__ i16x4 tr(const uint4* lds, int krow, int col) {
@@ -282,19 +240,40 @@ struct StageKm {
   }
 };
 
-template <bool KMAJ, int R>
-using Stage = typename std::conditional<KMAJ, StageKm<R>, StageKc<R>>::type;
+template <bool KMAJ, int R, int NT>
+using Stage = typename std::conditional<KMAJ, StageKm<R, NT>, StageKc<R, NT>>::type;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-  return __builtin_bit_cast(bf16x8, u);
-}
+// Explicit waits: the compiler's own waits know nothing of the direct
+// global -> LDS copies, and a plain __syncthreads would also drain them.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int TM, int TN>
+struct Frags {
+  bf16x8 a[TM], b[TN];
+};
 
 // ------------------------------------------------------------ MFMA kernel
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int STAGE_UNITS = (BM + BN) * 8;
+// NW waves, WGM of them along M; each wave owns (BM / WGM) x (BN / (NW / WGM))
+// outputs as TM x TN tiles of 32 x 32.  With 8 waves two share each SIMD, so
+// one wave's MFMAs run while the other waits on LDS or the barrier.
+// k-loop per 64-wide tile t: the next tile's direct copies are issued first;
+// then for each 16-wide k-step the fragments of the following step are read
+// from LDS while this step's MFMAs run; halfway through the last step every
+// wave waits for its copies of tile t + 1 and meets the barrier, so the
+// first fragments of tile t + 1 are read while the last MFMAs of tile t run.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int KK = BK / 16;
+  constexpr int SA_UNITS = BM * 8, STAGE_UNITS = (BM + BN) * 8;
   __shared__ uint4 lds[2 * STAGE_UNITS];
+  using SA = Stage<A_KMAJ, BM, NT>;
+  using SB = Stage<B_KMAJ, BN, NT>;
 
   int tm, tn;
   tile_coords(p, tm, tn);
@@ -302,11 +281,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
   const int kbeg = blockIdx.z * p.k_split;
   const int kend = min(p.K, kbeg + p.k_split);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = (wave & 1) * (BM / 2);
-  const int wn = (wave >> 1) * (BN / 2);
+  const int wm = (wave % WGM) * WM;
+  const int wn = (wave / WGM) * WN;
+  const int lrow = lane & 31;
+  const int lhalf = lane >> 5;
 
   // record counts: rows x leading dimension of each operand, in bytes
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
@@ -320,62 +300,104 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mfma(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  using SA = Stage<A_KMAJ, BM>;
-  using SB = Stage<B_KMAJ, BN>;
-  // tiles are copied global -> LDS asynchronously (no staging registers):
-  // tile kt+1 streams into the other buffer while tile kt is multiplied
-  if (nk > 0) {
-    SA::direct(lds, ra, p.lda, m0, p.M, kbeg, kend);
-    SB::direct(lds + BM * 8, rb, p.ldb, n0, p.N, kbeg, kend);
-  }
-  wait_lds_loads();
-  __syncthreads();
+  auto issue = [&](int t) {
+    uint4* st = lds + (t & 1) * STAGE_UNITS;
+    const int k0 = kbeg + t * BK;
+    SA::direct(st, ra, p.lda, m0, p.M, k0, kend);
+    SB::direct(st + SA_UNITS, rb, p.ldb, n0, p.N, k0, kend);
+  };
+  auto read = [&](Frags<TM, TN>& F, int t, int kk) {
+    const uint4* As = lds + (t & 1) * STAGE_UNITS;
+    const uint4* Bs = As + SA_UNITS;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) F.a[i] = SA::frag(As, wm + 32 * i + lrow, kk, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) F.b[j] = SB::frag(Bs, wn + 32 * j + lrow, kk, lane);
+  };
 
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      uint4* nxt = lds + (cur ^ 1) * STAGE_UNITS;
-      SA::direct(nxt, ra, p.lda, m0, p.M, k0, kend);
-      SB::direct(nxt + BM * 8, rb, p.ldb, n0, p.N, k0, kend);
+  Frags<TM, TN> F[2];
+  if constexpr (NW == 8) {
+    if (nk > 0) {
+      issue(0);
+      wait_loads();
+      block_barrier();
+      read(F[0], 0, 0);
     }
-    const uint4* As = lds + cur * STAGE_UNITS;
-    const uint4* Bs = As + BM * 8;
-    // fragments of k-step kk+1 are read while the MFMAs of step kk run
-    bf16x8 af[2][TM], bfr[2][TN];
+    for (int t = 0; t < nk; ++t) {
+      if (t + 1 < nk) issue(t + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = SA::frag(As, wm + 32 * i + lrow, 0, lane);
+      for (int kk = 0; kk < KK; ++kk) {
+        Frags<TM, TN>& cur = F[kk & 1];
+        Frags<TM, TN>& nxt = F[(kk + 1) & 1];
+        constexpr int NMF = TM * TN;
+        // MFMAs of this step issued before the fragment reads below: all of
+        // them, except on the last step, where half of them go first and the
+        // rest cover the barrier and the next tile's first reads
+        constexpr int FIRST = NMF / 2;
+        if (kk + 1 < KK) {
+          read(nxt, t, kk + 1);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = SB::frag(Bs, wn + 32 * j + lrow, 0, lane);
+          for (int q = 0; q < NMF; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cb = kk & 1;
-      if (kk + 1 < BK / 16) {
+          for (int q = 0; q < FIRST; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          // tile t + 1 has landed and every wave is done with stage t & 1
+          // (after the last tile this reads a stale stage that is never used)
+          wait_loads();
+          wait_lds();
+          block_barrier();
+          read(nxt, t + 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[cb ^ 1][i] = SA::frag(As, wm + 32 * i + lrow, kk + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[cb ^ 1][j] = SB::frag(Bs, wn + 32 * j + lrow, kk + 1, lane);
+          for (int q = FIRST; q < NMF; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
     }
-    wait_lds_loads();
+  } else {
+    // 4 waves (one per SIMD, two blocks per CU): reads and MFMAs of a tile
+    // are left to the compiler's schedule, the barrier closes the tile
+    if (nk > 0) issue(0);
+    wait_loads();
     __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+      if (t + 1 < nk) issue(t + 1);
+      read(F[0], t, 0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) read(F[(kk + 1) & 1], t, kk + 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[kk & 1].b[j], F[kk & 1].a[i], acc[j][i], 0, 0, 0);
+      }
+      wait_loads();
+      __syncthreads();
+    }
   }
+  wait_loads();
+  wait_lds();
+  block_barrier();
 
-  // Epilogue through LDS (free after the loop's last barrier): each wave
-  // writes one 32-row strip of its accumulators (lane: row lrow, columns
+  // Epilogue through LDS (free after the barrier above): each wave writes
+  // one 32-row strip of its accumulators (lane: row lrow, columns
   // 32 j + 8 g + 4 lhalf + e) and reads it back as 8-column row vectors, so
   // global reads and writes of the epilogue are contiguous 16-byte vectors.
-  constexpr int WN = BN / 2;              // columns per wave
   constexpr int PITCH = WN + 4;           // floats per staged row
   constexpr int LPR = WN / 8;             // lanes per row in the read-back
   constexpr int RPP = 64 / LPR;           // rows per pass
+  static_assert(NW * 32 * PITCH * 4 <= 2 * STAGE_UNITS * 16, "epilogue staging exceeds LDS");
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -514,10 +536,16 @@ Plan plan_mfma(const GemmDesc& d) {
   return pl;
 }
 
+// 256 x 256 tiles run 8 waves (two per SIMD, 128 x 64 each); the LM-head
+// statistics keep 4 waves so that a wave covers the 128 columns of one
+// (max, sum exp) partial.  128 x 128 tiles run 4 waves of 64 x 64.
 template <bool AK, bool BKm, int EPI, int BMv, int BNv>
 hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv>), grid, dim3(NTHREADS), 0, s, p);
+  if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
+    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
