@@ -401,10 +401,18 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
 
   if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, cs, s));
   RUN("norm1_fwd", launch_norm_fwd(ty, kind, d.N, C, x, w->ln1_w, opt(cfg, w->ln1_b), cfg->norm_eps, sv.a1, sv.stats1, s));
-  GemmDesc g = lin_fwd(d, sv.a1, C, w->w_qkv, 3 * C, EPI_STORE);
+  // RoPE / QK-norm ride in the QKV GEMM's epilogue when a wave's 128 output
+  // columns are exactly one head (bf16, head_dim 128); else a separate pass
+  const bool qk = cfg->rope || cfg->qk_norm;
+  const bool qk_fused = qk && ty == GPT_DTYPE_BF16 && d.D == 128;
+  GemmDesc g = lin_fwd(d, sv.a1, C, w->w_qkv, 3 * C, qk_fused ? EPI_QKNORM : EPI_STORE);
   g.out = sv.qkv; g.ldc = 3 * C; g.bias = opt(cfg, w->b_qkv);
+  if (qk_fused) {
+    g.qk_cs = cs; g.qk_rstd = sv.qkr; g.qk_T = T; g.qk_rope = cfg->rope; g.qk_norm = cfg->qk_norm;
+    g.qk_eps = cfg->norm_eps;
+  }
   RUN("qkv_gemm", launch_gemm(g, ty, nullptr, s));
-  if (cfg->rope || cfg->qk_norm)
+  if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
   RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, sv.qkv, sv.o, sv.lse, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
@@ -474,11 +482,18 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   RUN("out_wgrad", launch_gemm(lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate), ty, b.split, s));
   if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
   // attention
-  RUN("attn_delta", launch_attn_delta(ty, B, T, d.H, d.D, sv.o, b.dO, b.delta, s));
-  RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, s));
-  RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, s));
-  if (cfg->rope || cfg->qk_norm)
-    RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, b.cs, sv.qkv, sv.qkr, b.dqkv, s));
+  const QkBwd qk{cfg->rope, cfg->qk_norm, N, b.cs, sv.qkr};
+  if (attn_mfma_supported(ty, d.D)) {
+    // dQ pass first (it also forms delta); QK-norm / RoPE backward in both stores
+    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+  } else {
+    RUN("attn_delta", launch_attn_delta(ty, B, T, d.H, d.D, sv.o, b.dO, b.delta, s));
+    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+    if (cfg->rope || cfg->qk_norm)
+      RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, b.cs, sv.qkv, sv.qkr, b.dqkv, s));
+  }
   // fused QKV projection
   g = lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
   g.out = b.da; g.ldc = C;

@@ -326,6 +326,57 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   }
 }
 
+// QK-norm and RoPE backward applied to one row of a q or k gradient held as
+// MFMA accumulators g[dt][r] (column d = 32 dt + 8 (r / 4) + 4 hf + r % 4;
+// the two lane halves hold the two halves of the row).  y is the forward
+// output (normalised, rotated) row, r_inv its saved 1 / rms, t its position.
+// QK-norm: g <- r_inv (g - y mean(g * y)); RoPE: rotate pairs (i, i + D/2)
+// by -t theta_i.
+template <int D>
+__device__ __forceinline__ void qk_row_bwd(float (&g)[D / 32][16], const bf16* __restrict__ yrow, float r_inv,
+                                           const float2* __restrict__ cs_row, int hf, int rope, int qk_norm) {
+  constexpr int DT = D / 32;
+  if (qk_norm) {
+    float y[DT][16];
+    float part = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint2 u = *reinterpret_cast<const uint2*>(yrow + 32 * dt + 8 * q + 4 * hf);
+        y[dt][4 * q + 0] = __uint_as_float(u.x << 16);
+        y[dt][4 * q + 1] = __uint_as_float(u.x & 0xffff0000u);
+        y[dt][4 * q + 2] = __uint_as_float(u.y << 16);
+        y[dt][4 * q + 3] = __uint_as_float(u.y & 0xffff0000u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(g[dt][4 * q + e], y[dt][4 * q + e], part);
+      }
+    part += __shfl_xor(part, 32, 64);
+    const float m = part / D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) g[dt][r] = r_inv * (g[dt][r] - y[dt][r] * m);
+  }
+  if (rope) {
+#pragma unroll
+    for (int dt = 0; dt < DT / 2; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 32 * dt + 8 * q + 4 * hf;
+        const float4 c01 = *reinterpret_cast<const float4*>(cs_row + i);
+        const float4 c23 = *reinterpret_cast<const float4*>(cs_row + i + 2);
+        const float cc[4] = {c01.x, c01.z, c23.x, c23.z}, ss[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = g[dt][4 * q + e], b2 = g[dt + DT / 2][4 * q + e];
+          g[dt][4 * q + e] = a * cc[e] + b2 * ss[e];
+          g[dt + DT / 2][4 * q + e] = b2 * cc[e] - a * ss[e];
+        }
+      }
+  }
+}
+
 // ------------------------------------------------------ backward dK, dV (MFMA)
 template <int D>
 __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
@@ -333,7 +384,7 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
                                                              const float* __restrict__ lse,
                                                              const float* __restrict__ delta,
                                                              bf16* __restrict__ dqkv, float scale_log2,
-                                                             float scale) {
+                                                             float scale, QkBwd qk) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sQ[2][64 * KU];
   __shared__ uint4 sdO[2][64 * KU];
@@ -476,12 +527,30 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * hf;
         uint2 u;
-        u.x = pack2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale);
-        u.y = pack2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale);
-        *reinterpret_cast<uint2*>(krow + d) = u;
         u.x = pack2(dv[dt][4 * g], dv[dt][4 * g + 1]);
         u.y = pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
         *reinterpret_cast<uint2*>(vrow + d) = u;
+      }
+    float gk[DT][16];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gk[dt][r] = dk[dt][r] * scale;
+    if (qk.rope | qk.qk_norm) {
+      const long n = (long)b * T + kj;
+      const float r_inv = qk.qk_norm ? qk.rstd[(long)qk.N * H + n * H + h] : 1.0f;
+      qk_row_bwd<D>(gk, Kg + (long)kj * ld, r_inv, qk.rope ? qk.cs + (long)kj * (D / 2) : nullptr, hf, qk.rope,
+                     qk.qk_norm);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hf;
+        uint2 u;
+        u.x = pack2(gk[dt][4 * g], gk[dt][4 * g + 1]);
+        u.y = pack2(gk[dt][4 * g + 2], gk[dt][4 * g + 3]);
+        *reinterpret_cast<uint2*>(krow + d) = u;
       }
   }
 }
@@ -489,11 +558,12 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
 // ---------------------------------------------------------- backward dQ (MFMA)
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const bf16* __restrict__ qkv,
+                                                           const bf16* __restrict__ o,
                                                            const bf16* __restrict__ dO,
                                                            const float* __restrict__ lse,
-                                                           const float* __restrict__ delta,
+                                                           float* __restrict__ delta,
                                                            bf16* __restrict__ dqkv, float scale_log2,
-                                                           float scale) {
+                                                           float scale, QkBwd qk) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
@@ -525,7 +595,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   }
   const long row_lse = ((long)b * H + h) * T + qi;
   const float L2 = qi < T ? lse[row_lse] * LOG2E : 0.0f;
-  const float Dl = qi < T ? delta[row_lse] : 0.0f;
+  // delta = rowsum(dO * O) of this query from the same row slices df holds;
+  // the dK/dV pass, which runs next, reads it back
+  float Dl;
+  {
+    const __amdgpu_buffer_rsrc_t rOo = slice_rsrc(o + (long)b * T * C + h * D, T, C, D);
+    float part = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const bf16x8 ov = u4_bf8(bload(rOo, qi < T ? (uint32_t)(((long)qi * C + 16 * s2 + 8 * hf) * 2) : OOB));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[s2][e], part);
+    }
+    Dl = part + __shfl_xor(part, 32, 64);
+    if (qi < T && hf == 0) delta[row_lse] = Dl;
+  }
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -592,14 +676,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   }
   if (qi < T) {
     bf16* qrow = dqkv + ((long)b * T + qi) * ld + h * D;
+    float gq[DT][16];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gq[dt][r] = dq[dt][r] * scale;
+    if (qk.rope | qk.qk_norm) {
+      const long n = (long)b * T + qi;
+      const float r_inv = qk.qk_norm ? qk.rstd[n * H + h] : 1.0f;
+      qk_row_bwd<D>(gq, Qg + (long)qi * ld, r_inv, qk.rope ? qk.cs + (long)qi * (D / 2) : nullptr, hf, qk.rope,
+                     qk.qk_norm);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * hf;
         uint2 u;
-        u.x = pack2(dq[dt][4 * g] * scale, dq[dt][4 * g + 1] * scale);
-        u.y = pack2(dq[dt][4 * g + 2] * scale, dq[dt][4 * g + 3] * scale);
+        u.x = pack2(gq[dt][4 * g], gq[dt][4 * g + 1]);
+        u.y = pack2(gq[dt][4 * g + 2], gq[dt][4 * g + 3]);
         *reinterpret_cast<uint2*>(qrow + d) = u;
       }
   }
@@ -893,35 +988,35 @@ hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* 
 }
 
 hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
-                                const float* lse, const float* delta, void* dqkv, hipStream_t s) {
+                                const float* lse, const float* delta, void* dqkv, const QkBwd& qk, hipStream_t s) {
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
     dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale);
+                         delta, (bf16*)dqkv, scale_log2, scale, qk);
     else
       hipLaunchKernelGGL(attn_bwd_dkdv_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale);
+                         delta, (bf16*)dqkv, scale_log2, scale, qk);
     return hipGetLastError();
   }
   if (dtype == 1) return simt_dispatch<bf16>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
   return simt_dispatch<float>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
 }
 
-hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
-                              const float* lse, const float* delta, void* dqkv, hipStream_t s) {
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* o, const void* dO,
+                              const float* lse, float* delta, void* dqkv, const QkBwd& qk, hipStream_t s) {
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
     dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
-      hipLaunchKernelGGL(attn_bwd_dq_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale);
+      hipLaunchKernelGGL(attn_bwd_dq_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk);
     else
-      hipLaunchKernelGGL(attn_bwd_dq_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale);
+      hipLaunchKernelGGL(attn_bwd_dq_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)o,
+                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk);
     return hipGetLastError();
   }
   if (dtype == 1) return simt_dispatch<bf16>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);

@@ -271,7 +271,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int KK = BK / 16;
   constexpr int SA_UNITS = BM * 8, STAGE_UNITS = (BM + BN) * 8;
-  __shared__ uint4 lds[2 * STAGE_UNITS];
+  // the epilogue stages 32 rows x (WN + 4) floats per wave in the same LDS
+  constexpr int EPI_UNITS = NW * 32 * (WN + 4) / 4;
+  __shared__ uint4 lds[2 * STAGE_UNITS > EPI_UNITS ? 2 * STAGE_UNITS : EPI_UNITS];
   using SA = Stage<A_KMAJ, BM, NT>;
   using SB = Stage<B_KMAJ, BN, NT>;
 
@@ -397,7 +399,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
   constexpr int PITCH = WN + 4;           // floats per staged row
   constexpr int LPR = WN / 8;             // lanes per row in the read-back
   constexpr int RPP = 64 / LPR;           // rows per pass
-  static_assert(NW * 32 * PITCH * 4 <= 2 * STAGE_UNITS * 16, "epilogue staging exceeds LDS");
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -439,6 +440,45 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
         for (int o = LPR / 2; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
         if (m < p.M && lane % LPR == 0)
           p.part[(long)m * p.part_ld + p.part_off + (n0 + wn) / WN] = make_float2(mx, sm);
+      } else if constexpr (EPI == EPI_QKNORM) {
+        // the wave's 128 columns are one head of q, k or v (p.N = 3 C); a
+        // row is spread over 16 lanes of 8 columns, RoPE partners
+        // (i, i + 64) sit 8 lanes apart
+        static_assert(WN == 128, "fused RoPE / QK-norm needs one 128-wide head per wave");
+        const int C3 = p.N / 3;
+        const int which = (n0 + wn) / C3;
+        if (p.bias && n < p.N) {
+          float t8[8];
+          Vec8<bf16>::load(reinterpret_cast<const bf16*>(p.bias) + n, t8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += t8[e];
+        }
+        if (which < 2) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
+          const float r = p.qk_norm ? 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps) : 1.0f;
+          if (p.qk_rope) {
+            const int t = (m < p.M ? m : 0) % p.qk_T;
+            const bool lo = col < 64;
+            const float2* cs = p.qk_cs + (long)t * 64 + (col & 63);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float w2 = __shfl_xor(v[e], 8, 64);
+              const float2 c = cs[e];
+              v[e] = lo ? fmaf(v[e], c.x, -w2 * c.y) : fmaf(w2, c.y, v[e] * c.x);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= r;
+          if (p.qk_norm && (lane & 15) == 0 && m < p.M && n < p.N) {
+            const int H = C3 / 128;
+            p.qk_rstd[(long)which * p.M * H + (long)m * H + ((n0 + wn) % C3) / 128] = r;
+          }
+        }
+        if (m < p.M && n < p.N) Vec8<bf16>::store(reinterpret_cast<bf16*>(p.out) + (long)m * p.ldc + n, v);
       } else {
         epiW<bf16, EPI, 8>(p, m, n, v);
       }
@@ -519,7 +559,7 @@ struct Plan {
 Plan plan_mfma(const GemmDesc& d) {
   Plan pl;
   const long t256 = (long)cdiv(d.M, 256) * cdiv(d.N, 256);
-  if (d.epi == EPI_XENT_STATS || t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
+  if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM || t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else { pl.BMv = 128; pl.BNv = 128; }
   const long tiles = (long)cdiv(d.M, pl.BMv) * cdiv(d.N, pl.BNv);
   // split until the blocks cover the 256 CUs once (each split adds an fp32
@@ -536,13 +576,16 @@ Plan plan_mfma(const GemmDesc& d) {
   return pl;
 }
 
-// 256 x 256 tiles run 8 waves (two per SIMD, 128 x 64 each); the LM-head
+// 256 x 256 tiles run 8 waves (two per SIMD, 128 x 64 each, or 64 x 128 for
+// the fused RoPE / QK-norm epilogue, whose waves each hold one head); the LM-head
 // statistics keep 4 waves so that a wave covers the 128 columns of one
 // (max, sum exp) partial.  128 x 128 tiles run 4 waves of 64 x 64.
 template <bool AK, bool BKm, int EPI, int BMv, int BNv>
 hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
+  if constexpr (BMv == 256 && EPI == EPI_QKNORM)
+    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 4>), grid, dim3(512), 0, s, p);
+  else if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2>), grid, dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2>), grid, dim3(256), 0, s, p);
@@ -571,6 +614,8 @@ GemmParams make_params(const GemmDesc& d) {
   p.aux = d.aux; p.ldaux = d.ldaux; p.accumulate = d.accumulate;
   p.tgt = d.tgt; p.col_offset = d.col_offset; p.part = d.part; p.part_ld = d.part_ld;
   p.part_off = d.part_off; p.ztgt = d.ztgt; p.lse = d.lse; p.scale = d.scale;
+  p.qk_cs = d.qk_cs; p.qk_rstd = d.qk_rstd; p.qk_T = d.qk_T; p.qk_rope = d.qk_rope; p.qk_norm = d.qk_norm;
+  p.qk_eps = d.qk_eps;
   return p;
 }
 
@@ -638,6 +683,9 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
         break;
       case EPI_XENT_STATS:
         if (!ak && !bk) e = go_mfma<false, false, EPI_XENT_STATS, 256, 256>(p, pl.splits, s);
+        break;
+      case EPI_QKNORM:
+        if (!ak && !bk && d.N % 384 == 0) e = go_mfma<false, false, EPI_QKNORM, 256, 256>(p, pl.splits, s);
         break;
       case EPI_XENT_GRAD:
         if (!ak && !bk) e = go_mfma_tiles<false, false, EPI_XENT_GRAD>(p, pl, s);

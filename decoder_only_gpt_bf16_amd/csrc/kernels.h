@@ -20,6 +20,8 @@ enum EpiKind {
   EPI_F32 = 3,        // out(f32) = acc (+ out if accumulate)
   EPI_XENT_STATS = 4, // per (row, 128-col block): max and sum exp; target logit
   EPI_XENT_GRAD = 5,  // out(T) = (exp(acc - lse[m]) - [n + col_offset == tgt[m]]) * scale
+  EPI_QKNORM = 6,     // fused QKV (N = 3C, head_dim 128): out(T) = acc (+ bias), then RoPE and
+                      // QK-norm on the q and k heads; 1 / rms of each into qk_rstd [2][M][H]
 };
 
 struct GemmParams {
@@ -50,6 +52,11 @@ struct GemmParams {
   float* ztgt;            // [M] target logits
   const float* lse;       // [M]
   float scale;
+  // fused RoPE / QK-norm epilogue
+  const float2* qk_cs;    // [T][64] (cos, sin)
+  float* qk_rstd;
+  int qk_T, qk_rope, qk_norm;
+  float qk_eps;
 };
 
 struct GemmDesc {
@@ -65,6 +72,7 @@ struct GemmDesc {
   int accumulate;
   const int32_t* tgt; int col_offset; float2* part; int part_ld; int part_off;
   float* ztgt; const float* lse; float scale;
+  const float2* qk_cs; float* qk_rstd; int qk_T, qk_rope, qk_norm; float qk_eps;
 };
 
 // Bytes of split-K scratch launch_gemm may use for this problem (0 if none).
@@ -120,10 +128,21 @@ hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qk
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO,
                              float* delta, hipStream_t s);
 // Attention backward into the dk | dv thirds and the dq third of dqkv [N, 3C].
+// QK-norm / RoPE backward folded into the stores of dQ and dK (MFMA path).
+struct QkBwd {
+  int rope, qk_norm;
+  int N;                // B * T
+  const float2* cs;     // RoPE table [T][D / 2] of (cos, sin)
+  const float* rstd;    // saved 1 / rms of q then k, [2][N][H]
+};
+// MFMA path (attn_mfma_supported): run dQ first; it also writes delta for
+// the dK/dV pass, and both apply the QK-norm / RoPE backward of qk.  Other
+// paths: delta comes from launch_attn_delta, qk is ignored and
+// launch_qk_bwd follows.
 hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
-                                const float* lse, const float* delta, void* dqkv, hipStream_t s);
-hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
-                              const float* lse, const float* delta, void* dqkv, hipStream_t s);
+                                const float* lse, const float* delta, void* dqkv, const QkBwd& qk, hipStream_t s);
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* o, const void* dO,
+                              const float* lse, float* delta, void* dqkv, const QkBwd& qk, hipStream_t s);
 bool attn_mfma_supported(int dtype, int D);
 
 // Cross-entropy reductions.
