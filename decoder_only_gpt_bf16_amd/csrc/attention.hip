@@ -51,9 +51,11 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base, int T, long ld, int D) {
   return make_rsrc(base, ((long)(T - 1) * ld + D) * 2);
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  bf16 x = (bf16)a, y = (bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 // Pack accumulator registers 4g0..4g0+3 and 4g0+4..4g0+7 of a 32x32 tile as
 // the 8 bf16 k-slots of a B operand.
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       }
       // online softmax in the log2 domain; the causal mask is applied only on
       // tiles that cross the diagonal or the sequence end (uniform branch)
+      // raw scores; the log2-domain scale is folded into the exponent's FMA
       float p[2][16];
       auto scores = [&](auto masked) {
         float mx = -INFINITY;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float x = st[jt][r] * scale_log2;
+            float x = st[jt][r];
             if constexpr (decltype(masked)::value) {
               const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
               if (j > qi || j >= T) x = -INFINITY;
@@ -269,26 +272,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
       float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, mx * scale_log2);
       const bool dead = (m_new == -INFINITY);
-      const float corr = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float msub = dead ? 0.0f : m_new;
       float rs = 0.0f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(p[jt][r] - msub);
+          const float e = __builtin_amdgcn_exp2f(fmaf(p[jt][r], scale_log2, -msub));
           p[jt][r] = e;
           rs += e;
         }
       rs += __shfl_xor(rs, 32, 64);
-      l_run = l_run * corr + rs;
+      // rescale the running sums only when some row's maximum grew (a
+      // factor of exactly 1 otherwise)
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float corr = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+      }
+      l_run += rs;
       m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
       // O^T += V^T P^T; V^T fragments of step ks+1 are read during step ks
       bf16x8 vfr[2][DT];
 #pragma unroll
@@ -454,14 +462,17 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
     const bool more = t + 1 < t_end;
     const int qt0 = t * 64;
     if (more) stage_issue(t + 1, cur ^ 1);
-    if (qt0 + 63 >= kw && kw < T) {
+    {
       // the 64-query tile is processed as two 32-query halves: S = Q K^T and
       // dP = dO V^T for the half, P and dS, then dV^T += dO^T P and
-      // dK^T += Q^T dS over it; only one half's scores are live at a time
+      // dK^T += Q^T dS over it; only one half's scores are live at a time.
+      // Halves whose queries all precede the wave's keys are not skipped but
+      // masked to P = 0: the accumulators then follow one straight path (no
+      // register copies at the joins), and with one wave per SIMD the other
+      // waves of the block would wait at the barrier anyway
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int q0h = qt0 + 32 * it;
-        if (q0h + 31 < kw) continue;  // every query of this half precedes the wave's keys
         f32x16 S, dP;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { S[r] = 0.0f; dP[r] = 0.0f; }
