@@ -167,6 +167,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 //   k-major tiles, 256/512-byte rows:   f(r) = ((r & 3) << 2) | ((r >> 2) & 3)
 __device__ __forceinline__ int swz128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swzq(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+//   k-major tiles, 320-byte rows (20 units): f(r) = (r >> 2) & 3 (stays in range)
+template <int UPR>
+__device__ __forceinline__ int swz_km(int r) {
+  if constexpr (UPR == 20) return (r >> 2) & 3;
+  else return swzq(r);
+}
 
 // Asynchronous global -> LDS copy of 16 bytes per lane: lane L's vector
 // lands at LDS byte address lds_base + 16 L (lds_base wave-uniform); an
@@ -218,7 +224,7 @@ struct StageKm {
     for (int i = 0; i < NL; ++i) {
       const int P = (NT / 64 * i + w) * 64 + lane;
       const int kr = P / UPR;
-      const int c = (P % UPR) ^ swzq(kr);
+      const int c = (P % UPR) ^ swz_km<UPR>(kr);
       const int gk = k0 + kr, gc = r0 + 8 * c;
       const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
       load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
@@ -226,7 +232,7 @@ struct StageKm {
   }
   static __device__ __forceinline__ i16x4 tr(const uint4* lds, int krow, int col) {
     const bf16* base = reinterpret_cast<const bf16*>(lds);
-    const int off = (krow * UPR + ((col >> 3) ^ swzq(krow))) * 8 + (col & 7);
+    const int off = (krow * UPR + ((col >> 3) ^ swz_km<UPR>(krow))) * 8 + (col & 7);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + off));
   }
   // fragment of tile column `row` (an m or n index): k slots 16 kk + 8 hf + 0..7
@@ -397,8 +403,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
   // 32 j + 8 g + 4 lhalf + e) and reads it back as 8-column row vectors, so
   // global reads and writes of the epilogue are contiguous 16-byte vectors.
   constexpr int PITCH = WN + 4;           // floats per staged row
-  constexpr int LPR = WN / 8;             // lanes per row in the read-back
-  constexpr int RPP = 64 / LPR;           // rows per pass
+  constexpr int LPR = WN / 8;             // 8-column vectors (lanes) per row in the read-back
+  static_assert((32 * LPR) % 64 == 0, "read-back passes must cover whole rows");
+  static_assert((EPI != EPI_XENT_STATS && EPI != EPI_QKNORM) || 64 % LPR == 0,
+                "row reductions need a row's lanes in one pass");
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -409,9 +417,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
         *reinterpret_cast<float4*>(ep + lrow * PITCH + 32 * j + 8 * g + 4 * lhalf) =
             make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
     __builtin_amdgcn_wave_barrier();
-    const int col = (lane % LPR) * 8;
-    for (int pass = 0; pass < 32 / RPP; ++pass) {
-      const int row = pass * RPP + lane / LPR;
+    for (int pass = 0; pass < 32 * LPR / 64; ++pass) {
+      const int item = pass * 64 + lane;
+      const int row = item / LPR;
+      const int col = (item % LPR) * 8;
       float v[8];
       const float4 a = *reinterpret_cast<const float4*>(ep + row * PITCH + col);
       const float4 b = *reinterpret_cast<const float4*>(ep + row * PITCH + col + 4);
@@ -559,7 +568,9 @@ struct Plan {
 Plan plan_mfma(const GemmDesc& d) {
   Plan pl;
   const long t256 = (long)cdiv(d.M, 256) * cdiv(d.N, 256);
+  const long t160 = (long)cdiv(d.M, 256) * cdiv(d.N, 160);
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM || t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
+  else if (d.N % 160 == 0 && t160 >= 240 && t160 % 256 <= 16) { pl.BMv = 256; pl.BNv = 160; }
   else { pl.BMv = 128; pl.BNv = 128; }
   const long tiles = (long)cdiv(d.M, pl.BMv) * cdiv(d.N, pl.BNv);
   // split until the blocks cover the 256 CUs once (each split adds an fp32
@@ -592,9 +603,20 @@ hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 256 x 160 tiles (N a multiple of 160, e.g. 1280 = 8 x 160 with M = 8192:
+// exactly one tile per CU) run 4 waves of 64 x 160.
 template <bool AK, bool BKm, int EPI>
 hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
-  if (pl.BMv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
+  if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
+  if (pl.BNv == 160) {
+    if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM) {
+      return hipErrorInvalidValue;
+    } else {
+      dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 160, 4, 4>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   return go_mfma<AK, BKm, EPI, 128, 128>(p, pl.splits, s);
 }
 

@@ -65,12 +65,12 @@ __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restr
 
 // dx = norm backward (+ resid); column partials of dy*xhat (gain) and dy
 // (bias) per block into colpart[0][blk][C], colpart[1][blk][C].
-template <typename T, int KIND>
+template <typename T, int KIND, bool COLS>
 __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restrict__ x,
                                                   const T* __restrict__ w, const T* __restrict__ dy,
                                                   const T* __restrict__ resid, float eps,
-                                                  T* __restrict__ dx, float* __restrict__ colpart,
-                                                  int want_cols) {
+                                                  T* __restrict__ dx, float* __restrict__ colpart) {
+  constexpr bool want_cols = COLS;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   float cw[MAX_VPL][8], cb[MAX_VPL][8];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
       }
     }
   }
-  if (!want_cols) return;
+  if constexpr (!COLS) return;
   // reduce the 4 waves' column partials through LDS, fixed order
   __shared__ float red[ROWS_PER_BLOCK][2][64 * 8];
 #pragma unroll
@@ -209,10 +209,16 @@ hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, con
                            float* colpart, int want_cols, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   dim3 grid(norm_bwd_blocks(N)), block(256);
-#define NB(T, K) hipLaunchKernelGGL((norm_bwd_k<T, K>), grid, block, 0, s, N, C, (const T*)x, \
-                                    (const T*)w, (const T*)dy, (const T*)resid, eps, (T*)dx, colpart, want_cols)
-  if (dtype == 1) { if (kind == 0) NB(bf16, 0); else NB(bf16, 1); }
-  else { if (kind == 0) NB(float, 0); else NB(float, 1); }
+#define NB(T, K, COLS) hipLaunchKernelGGL((norm_bwd_k<T, K, COLS>), grid, block, 0, s, N, C, (const T*)x, \
+                                          (const T*)w, (const T*)dy, (const T*)resid, eps, (T*)dx, colpart)
+  // column partials exist only for LayerNorm's gain and bias
+  if (dtype == 1) {
+    if (kind == 0) { if (want_cols) NB(bf16, 0, true); else NB(bf16, 0, false); }
+    else NB(bf16, 1, false);
+  } else {
+    if (kind == 0) { if (want_cols) NB(float, 0, true); else NB(float, 0, false); }
+    else NB(float, 1, false);
+  }
 #undef NB
   return hipGetLastError();
 }
