@@ -60,6 +60,8 @@ def site_work(name, B, T, C, H):
         "fc_gemm_gelu": g(N, 4 * C, C), "fc_dgrad": g(N, C, 4 * C), "fc_wgrad": g(4 * C, C, N),
         "proj_gemm": g(N, C, 4 * C), "proj_dgrad_gelu": g(N, 4 * C, C), "proj_wgrad": g(C, 4 * C, N),
         "attn_fwd": 2 * half, "attn_bwd_dkdv": 3 * half, "attn_bwd_dq": 1 * half,
+        # the four weight gradients as one grouped launch
+        "wgrad_group": g(3 * C, C, N) + g(C, C, N) + g(4 * C, C, N) + g(C, 4 * C, N),
     }
     if name in flops:
         return "mfma", flops[name]

@@ -462,12 +462,17 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   GemmDesc g = lin_dgrad(d, dy, C, w->w_proj, 4 * C, EPI_GELU_BWD);
   g.out = b.du; g.ldc = 4 * C; g.aux = sv.u; g.ldaux = 4 * C;
   RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
-  RUN("proj_wgrad", launch_gemm(lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate), ty, b.split, s));
+  // weight gradients depend on nothing computed later: they are gathered and
+  // run as one grouped launch at the end of the backward (one launch fills
+  // the machine where each alone would leave CUs idle)
+  GemmDesc wg[GEMM_GROUP_MAX];
+  int nwg = 0;
+  wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
   if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
   g = lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
-  RUN("fc_wgrad", launch_gemm(lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate), ty, b.split, s));
+  wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
   if (cfg->bias) RUN("fc_bias", launch_colsum(ty, N, 4 * C, 4 * C, b.du, gr->b_fc, accumulate, b.colsum, s));
   // norm 2 backward + residual
   RUN("norm2_bwd", launch_norm_bwd(ty, kind, N, C, sv.x1, w->ln2_w, b.da, dy, cfg->norm_eps, b.dx1, b.colpart, ln, s));
@@ -479,7 +484,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   g = lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
   g.out = b.dO; g.ldc = C;
   RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
-  RUN("out_wgrad", launch_gemm(lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate), ty, b.split, s));
+  wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
   if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
   // attention
   const QkBwd qk{cfg->rope, cfg->qk_norm, N, b.cs, sv.qkr};
@@ -498,7 +503,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   g = lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
-  RUN("qkv_wgrad", launch_gemm(lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate), ty, b.split, s));
+  wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);
   if (cfg->bias) RUN("qkv_bias", launch_colsum(ty, N, 3 * C, 3 * C, b.dqkv, gr->b_qkv, accumulate, b.colsum, s));
   // norm 1 backward + residual
   RUN("norm1_bwd", launch_norm_bwd(ty, kind, N, C, x, w->ln1_w, b.da, b.dx1, cfg->norm_eps, dx, b.colpart, ln, s));
@@ -506,6 +511,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln1_w, accumulate, s));
     if (cfg->bias) RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln1_b, accumulate, s));
   }
+  RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, s));
   return GPT_OK;
 }
 

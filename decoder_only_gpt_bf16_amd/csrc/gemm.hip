@@ -127,9 +127,8 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
 }
 
 // Block id -> (tile_m, tile_n): XCD-aware remap, then grouped ordering.
-__device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
-  const int nb = gridDim.x;
-  int b = blockIdx.x;
+__device__ __forceinline__ void tile_coords(const GemmParams& p, int bid, int nb, int& tm, int& tn) {
+  int b = bid;
   {
     const int xcd = b & 7, idx = b >> 3;
     const int per = nb >> 3, rem = nb & 7;
@@ -270,7 +269,7 @@ struct Frags {
 // wave waits for its copies of tile t + 1 and meets the barrier, so the
 // first fragments of tile t + 1 are read while the last MFMAs of tile t run.
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int bid, int nb) {
   constexpr int NT = NW * 64;
   constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
   using SB = Stage<B_KMAJ, BN, NT>;
 
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, bid, nb, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = blockIdx.z * p.k_split;
   const int kend = min(p.K, kbeg + p.k_split);
@@ -494,6 +493,28 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
+  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, blockIdx.x, gridDim.x);
+}
+
+// Several independent problems of one kind in a single launch: blocks
+// [start[q], start[q + 1]) compute the tiles of problem q.
+struct GemmGroup {
+  GemmParams p[GEMM_GROUP_MAX];
+  int start[GEMM_GROUP_MAX + 1];
+  int count;
+};
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_mfma_group(GemmGroup g) {
+  int q = 0;
+#pragma unroll
+  for (int i = 1; i < GEMM_GROUP_MAX; ++i)
+    if (i < g.count && (int)blockIdx.x >= g.start[i]) q = i;
+  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(g.p[q], blockIdx.x - g.start[q], g.start[q + 1] - g.start[q]);
 }
 
 // ------------------------------------------------------------ SIMT kernel
@@ -754,4 +775,37 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
       break;
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, hipStream_t s) {
+  bool ok = n > 0 && n <= GEMM_GROUP_MAX && dtype == 1;
+  uint32_t ab[GEMM_GROUP_MAX] = {}, bb[GEMM_GROUP_MAX] = {};
+  for (int i = 0; ok && i < n; ++i)
+    ok = d[i].epi == EPI_F32 && d[i].a_kmaj && d[i].b_kmaj && d[i].M > 0 && d[i].N > 0 && mfma_ok(d[i], ab[i], bb[i]);
+  if (!ok) {
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = launch_gemm(d[i], dtype, ws, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  // 128 x 128 tiles (4 waves, two blocks per CU) for every problem; with
+  // both operands k-major they measured faster than 256 x 160
+  GemmGroup g{};
+  g.count = n;
+  int total = 0;
+  for (int i = 0; i < n; ++i) {
+    GemmParams p = make_params(d[i]);
+    p.tiles_m = cdiv(d[i].M, 128);
+    p.tiles_n = cdiv(d[i].N, 128);
+    p.k_split = d[i].K;
+    p.a_bytes = ab[i];
+    p.b_bytes = bb[i];
+    g.p[i] = p;
+    g.start[i] = total;
+    total += p.tiles_m * p.tiles_n;
+  }
+  for (int i = n; i <= GEMM_GROUP_MAX; ++i) g.start[i] = total;
+  hipLaunchKernelGGL((gemm_mfma_group<true, true, EPI_F32, 128, 128, 4, 2>), dim3(total), dim3(256), 0, s, g);
+  return hipGetLastError();
 }

@@ -81,6 +81,11 @@ size_t gemm_split_scratch_bytes(const GemmDesc& d, int dtype);
 int xent_part_cols();
 // Launch; `ws` provides split-K scratch of gemm_split_scratch_bytes().
 hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s);
+// Up to GEMM_GROUP_MAX independent fp32-output (EPI_F32) problems with both
+// operands k-major (weight gradients) in one launch, no split-K; falls back
+// to one launch_gemm each when the problems cannot share a tile shape.
+constexpr int GEMM_GROUP_MAX = 4;
+hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Norms, embeddings, attention, cross-entropy, reductions.
