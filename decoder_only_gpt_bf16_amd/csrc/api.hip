@@ -130,7 +130,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // ------------------------------------------------------------ block layouts
 struct Saved {
-  void *a1, *qkv, *o, *x1, *a2, *u, *g;
+  void *a1, *qkv, *o, *x1, *a2, *u, *g;  // u holds GELU'(fc output), g = GELU(fc output)
   float *stats1, *stats2, *qkr, *lse;
 };
 

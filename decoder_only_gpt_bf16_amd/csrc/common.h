@@ -69,8 +69,9 @@ template <> struct Vec8<float> {
 // erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
 // erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 // t = 1 / (1 + p x) for x >= 0 (odd extension), |error| <= 1.5e-7.
-// Inline arithmetic (one exp, one reciprocal) so GEMM epilogues make no calls.
-__device__ __forceinline__ float erf_as(float x) {
+// Inline arithmetic (one exp, one reciprocal) so GEMM epilogues make no
+// calls; e receives exp(-x^2).
+__device__ __forceinline__ float erf_as(float x, float& e) {
   const float ax = fabsf(x);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
   float poly = fmaf(1.061405429f, t, -1.453152027f);
@@ -78,20 +79,18 @@ __device__ __forceinline__ float erf_as(float x) {
   poly = fmaf(poly, t, -0.284496736f);
   poly = fmaf(poly, t, 0.254829592f);
   poly *= t;
-  const float e = __expf(-ax * ax);
-  const float r = fmaf(-poly, e, 1.0f);
-  return copysignf(r, x);
+  e = __expf(-ax * ax);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
 }
 
-// GELU with the exact (erf) form, u * Phi(u), and its derivative
-// Phi(u) + u * phi(u).
-__device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f));
-}
-__device__ __forceinline__ float gelu_grad_f(float u) {
-  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f));
-  const float pdf = __expf(-0.5f * u * u) * 0.39894228040143268f;
-  return fmaf(u, pdf, cdf);
+// GELU with the exact (erf) form, g = u Phi(u), and its derivative
+// dg = Phi(u) + u phi(u), from one erf evaluation: with x = u / sqrt 2 the
+// exponential of the erf formula is exp(-u^2 / 2) = sqrt(2 pi) phi(u).
+__device__ __forceinline__ void gelu_and_grad(float u, float& g, float& dg) {
+  float e;
+  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f, e));
+  g = u * cdf;
+  dg = fmaf(u, e * 0.39894228040143268f, cdf);
 }
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }

@@ -93,16 +93,18 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
       for (int e = 0; e < W; ++e) v[e] += t[e];
     }
   } else if constexpr (EPI == EPI_GELU) {
+    // out2 = GELU(u) feeds the next GEMM; out = GELU'(u) is what the
+    // backward needs of u, so it is stored in u's place
     float g[W];
-    for (int e = 0; e < W; ++e) g[e] = gelu_f(v[e]);
+    for (int e = 0; e < W; ++e) gelu_and_grad(v[e], g[e], v[e]);
     T* o2 = reinterpret_cast<T*>(p.out2) + (long)m * p.ldc + n;
     if (full) storeW<T, W>(o2, g);
     else for (int e = 0; e < W; ++e) if (n + e < p.N) o2[e] = from_f32<T>(g[e]);
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    const T* u = reinterpret_cast<const T*>(p.aux) + (long)m * p.ldaux + n;
-    if (full) loadW<T, W>(u, t);
-    else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(u[e]) : 0.0f;
-    for (int e = 0; e < W; ++e) v[e] *= gelu_grad_f(t[e]);
+    const T* dg = reinterpret_cast<const T*>(p.aux) + (long)m * p.ldaux + n;
+    if (full) loadW<T, W>(dg, t);
+    else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(dg[e]) : 0.0f;
+    for (int e = 0; e < W; ++e) v[e] *= t[e];
   } else if constexpr (EPI == EPI_XENT_GRAD) {
     const float l = p.lse[m];
     const int tg = p.tgt[m] - p.col_offset;
