@@ -189,15 +189,19 @@ GemmDesc lin_wgrad(const Dims& d, const void* dY, int Out, const void* X, int In
   return g;
 }
 
+// the block's four weight gradients, in the order the backward forms them
+void block_wgrads(const Dims& d, GemmDesc* wg) {
+  const int C = d.C;
+  wg[0] = lin_wgrad(d, nullptr, C, nullptr, 4 * C, nullptr, 0);   // proj
+  wg[1] = lin_wgrad(d, nullptr, 4 * C, nullptr, C, nullptr, 0);   // fc
+  wg[2] = lin_wgrad(d, nullptr, C, nullptr, C, nullptr, 0);       // out
+  wg[3] = lin_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0);   // qkv
+}
+
 size_t split_need(const Dims& d) {
-  const size_t C = d.C;
-  size_t m = 0;
-  GemmDesc g;
-  g = lin_wgrad(d, nullptr, C, nullptr, 4 * C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
-  g = lin_wgrad(d, nullptr, 4 * C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
-  g = lin_wgrad(d, nullptr, C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
-  g = lin_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0); m = std::max(m, gemm_split_scratch_bytes(g, d.dtype));
-  return m;
+  GemmDesc wg[4];
+  block_wgrads(d, wg);
+  return gemm_group_scratch_bytes(wg, 4, d.dtype);
 }
 
 BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
@@ -511,7 +515,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln1_w, accumulate, s));
     if (cfg->bias) RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln1_b, accumulate, s));
   }
-  RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, s));
+  RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, split_need(d), s));
   return GPT_OK;
 }
 

@@ -270,8 +270,12 @@ struct Frags {
 // from LDS while this step's MFMAs run; halfway through the last step every
 // wave waits for its copies of tile t + 1 and meets the barrier, so the
 // first fragments of tile t + 1 are read while the last MFMAs of tile t run.
+// One output tile (tm, tn) over k in [kbeg, kend).  part == nullptr: the
+// epilogue of EPI; else the raw fp32 accumulators go to part as a dense
+// BM x BN tile (a partial sum for a later fixed-order reduction).
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, int bid, int nb) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, int kbeg, int kend,
+                                          float* __restrict__ part) {
   constexpr int NT = NW * 64;
   constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -284,11 +288,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bid, int nb) 
   using SA = Stage<A_KMAJ, BM, NT>;
   using SB = Stage<B_KMAJ, BN, NT>;
 
-  int tm, tn;
-  tile_coords(p, bid, nb, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = blockIdx.z * p.k_split;
-  const int kend = min(p.K, kbeg + p.k_split);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -490,7 +490,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bid, int nb) 
         }
         if (m < p.M && n < p.N) Vec8<bf16>::store(reinterpret_cast<bf16*>(p.out) + (long)m * p.ldc + n, v);
       } else {
-        epiW<bf16, EPI, 8>(p, m, n, v);
+        if (part) {
+          float* d = part + (long)(m - m0) * BN + (n - n0);
+          reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          epiW<bf16, EPI, 8>(p, m, n, v);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -499,24 +505,108 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int bid, int nb) 
 
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
-  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, blockIdx.x, gridDim.x);
+  int tm, tn;
+  tile_coords(p, blockIdx.x, gridDim.x, tm, tn);
+  const int kbeg = blockIdx.z * p.k_split;
+  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, tm, tn, kbeg, min(p.K, kbeg + p.k_split), nullptr);
 }
 
 // Several independent problems of one kind in a single launch: blocks
-// [start[q], start[q + 1]) compute the tiles of problem q.
+// [start[q], start[q + 1]) cover the tiles of problem q.
 struct GemmGroup {
   GemmParams p[GEMM_GROUP_MAX];
   int start[GEMM_GROUP_MAX + 1];
   int count;
 };
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_mfma_group(GemmGroup g) {
-  int q = 0;
+// Grouped problems that share K, as "data-parallel + stream-K": with T
+// tiles over G blocks, block b first computes whole tiles b, b + G, ...
+// (R = T / G of them); the k-steps of the remaining T - R G tiles are then
+// split evenly over the G blocks, each writing its piece of a tile as an fp32
+// partial into slot (tile, piece) for streamk_fixup to add in order.
+struct StreamKPlan {
+  int G;          // blocks
+  int R;          // whole tiles per block
+  int nk;         // k-steps (of BK) per tile
+  int rem;        // tiles left for the split phase
+  int S;          // partial slots per split tile
+  float* part;    // [rem][S][BM * BN]
+};
+
+__host__ __device__ inline long sk_units_begin(const StreamKPlan& k, int b) {
+  return (long)b * k.rem * k.nk / k.G;
+}
+// the block whose split-phase range holds unit u
+__host__ __device__ inline int sk_block_of(const StreamKPlan& k, long u) {
+  int b = (int)(u * k.G / ((long)k.rem * k.nk));
+  while (b + 1 < k.G && sk_units_begin(k, b + 1) <= u) ++b;
+  while (b > 0 && sk_units_begin(k, b) > u) --b;
+  return b;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void group_tile(const GemmGroup& g, int tile, int& q, int& tm, int& tn) {
+  q = 0;
 #pragma unroll
   for (int i = 1; i < GEMM_GROUP_MAX; ++i)
-    if (i < g.count && (int)blockIdx.x >= g.start[i]) q = i;
-  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(g.p[q], blockIdx.x - g.start[q], g.start[q + 1] - g.start[q]);
+    if (i < g.count && tile >= g.start[i]) q = i;
+  tile_coords(g.p[q], tile - g.start[q], g.start[q + 1] - g.start[q], tm, tn);
+}
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_streamk(GemmGroup g, StreamKPlan k) {
+  const int b = blockIdx.x;
+  int q, tm, tn;
+  for (int r = 0; r < k.R; ++r) {
+    group_tile<BM, BN>(g, r * k.G + b, q, tm, tn);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(g.p[q], tm, tn, 0, g.p[q].K, nullptr);
+    block_barrier();  // the epilogue's LDS staging is done before the next prologue
+  }
+  if (k.rem == 0) return;
+  const long u1 = sk_units_begin(k, b + 1);
+  for (long u = sk_units_begin(k, b); u < u1;) {
+    const int rt = (int)(u / k.nk);                 // split-phase tile
+    const int k0 = (int)(u % k.nk);
+    const int k1 = (int)min((long)k.nk, k0 + (u1 - u));
+    group_tile<BM, BN>(g, k.R * k.G + rt, q, tm, tn);
+    const GemmParams& p = g.p[q];
+    float* part = nullptr;
+    if (k0 != 0 || k1 != k.nk) {
+      const int first = sk_block_of(k, (long)rt * k.nk);
+      part = k.part + ((long)rt * k.S + (b - first)) * (BM * BN);
+    }
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, tm, tn, k0 * BK, min(p.K, k1 * BK), part);
+    block_barrier();
+    u += k1 - k0;
+  }
+}
+
+// Adds the partial slots of each split-phase tile in piece order (fixed
+// order: bitwise reproducible) and writes the fp32 result (+= when the
+// problem accumulates).  One block per (tile, 256 x 8-column group).
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void streamk_fixup(GemmGroup g, StreamKPlan k) {
+  const int rt = blockIdx.y;
+  const int first = sk_block_of(k, (long)rt * k.nk);
+  const int last = sk_block_of(k, (long)(rt + 1) * k.nk - 1);
+  if (first == last) return;  // one block computed it whole
+  int q, tm, tn;
+  group_tile<BM, BN>(g, k.R * k.G + rt, q, tm, tn);
+  const GemmParams& p = g.p[q];
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // element within the tile
+  if (e >= BM * BN) return;
+  const int r = e / BN, c = e % BN;
+  const int m = tm * BM + r, n = tn * BN + c;
+  if (m >= p.M || n >= p.N) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j <= last - first; ++j) {
+    const float4 v = *reinterpret_cast<const float4*>(k.part + ((long)rt * k.S + j) * (BM * BN) + e);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  float* o = reinterpret_cast<float*>(p.out) + (long)m * p.ldc + n;
+  const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+  for (int t = 0; t < 4; ++t)
+    if (n + t < p.N) o[t] = p.accumulate ? o[t] + a4[t] : a4[t];
 }
 
 // ------------------------------------------------------------ SIMT kernel
@@ -779,35 +869,72 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, hipStream_t s) {
-  bool ok = n > 0 && n <= GEMM_GROUP_MAX && dtype == 1;
-  uint32_t ab[GEMM_GROUP_MAX] = {}, bb[GEMM_GROUP_MAX] = {};
-  for (int i = 0; ok && i < n; ++i)
-    ok = d[i].epi == EPI_F32 && d[i].a_kmaj && d[i].b_kmaj && d[i].M > 0 && d[i].N > 0 && mfma_ok(d[i], ab[i], bb[i]);
-  if (!ok) {
-    for (int i = 0; i < n; ++i) {
-      hipError_t e = launch_gemm(d[i], dtype, ws, s);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
-  // 128 x 128 tiles (4 waves, two blocks per CU) for every problem; with
-  // both operands k-major they measured faster than 256 x 160
-  GemmGroup g{};
+// Stream-K plan of a weight-gradient group: 256 x 256 tiles over
+// SK_BLOCKS blocks (the CU count of an MI355X).  Returns false when the
+// problems do not qualify (bf16 MFMA operands, both k-major, fp32 output,
+// one K that is a multiple of BK).
+constexpr int SK_BLOCKS = 256;
+static bool streamk_plan(const GemmDesc* d, int n, int dtype, GemmGroup& g, StreamKPlan& k, size_t& scratch) {
+  if (n <= 0 || n > GEMM_GROUP_MAX || dtype != 1) return false;
+  const int K = d[0].K;
+  if (K <= 0 || K % BK) return false;
+  g = GemmGroup{};
   g.count = n;
   int total = 0;
   for (int i = 0; i < n; ++i) {
+    uint32_t ab = 0, bb = 0;
+    if (d[i].epi != EPI_F32 || !d[i].a_kmaj || !d[i].b_kmaj || d[i].K != K || d[i].M <= 0 || d[i].N <= 0 ||
+        !mfma_ok(d[i], ab, bb))
+      return false;
     GemmParams p = make_params(d[i]);
-    p.tiles_m = cdiv(d[i].M, 128);
-    p.tiles_n = cdiv(d[i].N, 128);
-    p.k_split = d[i].K;
-    p.a_bytes = ab[i];
-    p.b_bytes = bb[i];
+    p.tiles_m = cdiv(d[i].M, 256);
+    p.tiles_n = cdiv(d[i].N, 256);
+    p.k_split = K;
+    p.a_bytes = ab;
+    p.b_bytes = bb;
     g.p[i] = p;
     g.start[i] = total;
     total += p.tiles_m * p.tiles_n;
   }
   for (int i = n; i <= GEMM_GROUP_MAX; ++i) g.start[i] = total;
-  hipLaunchKernelGGL((gemm_mfma_group<true, true, EPI_F32, 128, 128, 4, 2>), dim3(total), dim3(256), 0, s, g);
-  return hipGetLastError();
+  k = StreamKPlan{};
+  k.G = SK_BLOCKS;
+  k.R = total / k.G;
+  k.rem = total % k.G;
+  k.nk = K / BK;
+  k.S = 1;
+  for (int rt = 0; rt < k.rem; ++rt)
+    k.S = std::max(k.S, sk_block_of(k, (long)(rt + 1) * k.nk - 1) - sk_block_of(k, (long)rt * k.nk) + 1);
+  scratch = k.rem ? align256((size_t)k.rem * k.S * 256 * 256 * sizeof(float)) : 0;
+  return true;
+}
+
+size_t gemm_group_scratch_bytes(const GemmDesc* d, int n, int dtype) {
+  GemmGroup g;
+  StreamKPlan k;
+  size_t need = 0;
+  if (streamk_plan(d, n, dtype, g, k, need)) return need;
+  size_t m = 0;
+  for (int i = 0; i < n; ++i) m = std::max(m, gemm_split_scratch_bytes(d[i], dtype));
+  return m;
+}
+
+hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s) {
+  GemmGroup g;
+  StreamKPlan k;
+  size_t need = 0;
+  if (streamk_plan(d, n, dtype, g, k, need) && (need == 0 || (ws && ws_bytes >= need))) {
+    k.part = static_cast<float*>(ws);
+    hipLaunchKernelGGL((gemm_streamk<true, true, EPI_F32, 256, 256, 8, 2>), dim3(k.G), dim3(512), 0, s, g, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || k.rem == 0) return e;
+    hipLaunchKernelGGL((streamk_fixup<256, 256>), dim3(256 * 256 / 1024, k.rem), dim3(256), 0, s, g, k);
+    return hipGetLastError();
+  }
+  // otherwise one launch per problem
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = launch_gemm(d[i], dtype, ws, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }

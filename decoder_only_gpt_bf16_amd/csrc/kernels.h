@@ -82,10 +82,13 @@ int xent_part_cols();
 // Launch; `ws` provides split-K scratch of gemm_split_scratch_bytes().
 hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s);
 // Up to GEMM_GROUP_MAX independent fp32-output (EPI_F32) problems with both
-// operands k-major (weight gradients) in one launch, no split-K; falls back
-// to one launch_gemm each when the problems cannot share a tile shape.
+// operands k-major and one K (the weight gradients of a block) as one
+// stream-K launch plus a fixed-order fixup of the tiles split between
+// blocks; falls back to one launch_gemm each.  `ws` must hold
+// gemm_group_scratch_bytes() bytes.
 constexpr int GEMM_GROUP_MAX = 4;
-hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, hipStream_t s);
+size_t gemm_group_scratch_bytes(const GemmDesc* d, int n, int dtype);
+hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Norms, embeddings, attention, cross-entropy, reductions.
