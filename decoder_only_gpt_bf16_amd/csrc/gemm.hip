@@ -374,13 +374,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
       }
     }
   } else {
-    // 4 waves (one per SIMD, two blocks per CU): reads and MFMAs of a tile
-    // are left to the compiler's schedule, the barrier closes the tile
+    // 4 waves (one per SIMD): reads and MFMAs of a tile are left to the
+    // compiler's schedule, the barrier closes the tile
     if (nk > 0) issue(0);
     wait_loads();
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
       if (t + 1 < nk) issue(t + 1);
+      // LLVM's igrouplp strategy 0 interleaves the LDS reads with the MFMAs;
+      // measured faster with a k-major B operand (transposed reads), slower
+      // with a k-contiguous one
+      if constexpr (B_KMAJ) __builtin_amdgcn_iglp_opt(0);
       read(F[0], t, 0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
