@@ -169,10 +169,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swzq(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 //   k-major tiles, 320-byte rows (20 units): f(r) = (r >> 2) & 3 (stays in range)
+//   k-major tiles, 640-byte rows (40 units): f(r) = tab[r & 15] < 8, found by
+//   search over such tables
 template <int UPR>
 __device__ __forceinline__ int swz_km(int r) {
-  if constexpr (UPR == 20) return (r >> 2) & 3;
-  else return swzq(r);
+  if constexpr (UPR == 20) {
+    return (r >> 2) & 3;
+  } else if constexpr (UPR == 40) {
+    constexpr uint64_t tab = 0x6433054362356005ull;  // nibble i = f(i): 5,0,0,6,5,3,2,6,3,4,5,0,3,3,4,6
+    return (int)((tab >> (4 * (r & 15))) & 0xf);
+  } else {
+    return swzq(r);
+  }
 }
 
 // Asynchronous global -> LDS copy of 16 bytes per lane: lane L's vector
@@ -282,8 +290,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int KK = BK / 16;
   constexpr int SA_UNITS = BM * 8, STAGE_UNITS = (BM + BN) * 8;
-  // the epilogue stages 32 rows x (WN + 4) floats per wave in the same LDS
-  constexpr int EPI_UNITS = NW * 32 * (WN + 4) / 4;
+  // the epilogue stages SR rows x (WN + 4) floats per wave in the same LDS
+  // (32 rows, or 16 when 32 would not fit in the 160 KB of a CU)
+  constexpr int SR = NW * 32 * (WN + 4) * 4 <= 160 * 1024 ? 32 : 16;
+  constexpr int EPI_UNITS = NW * SR * (WN + 4) / 4;
   __shared__ uint4 lds[2 * STAGE_UNITS > EPI_UNITS ? 2 * STAGE_UNITS : EPI_UNITS];
   using SA = Stage<A_KMAJ, BM, NT>;
   using SB = Stage<B_KMAJ, BN, NT>;
@@ -325,7 +335,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   };
 
   Frags<TM, TN> F[2];
-  if constexpr (NW == 8) {
+  // the explicit pipeline keeps two fragment sets live; wide 8-wave tiles
+  // (64 x 160 per wave) cannot afford them and use the compiler's schedule
+  constexpr bool PIPE = NW == 8 && TM * TN <= 8;
+  if constexpr (PIPE) {
     if (nk > 0) {
       issue(0);
       wait_loads();
@@ -374,8 +387,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
       }
     }
   } else {
-    // 4 waves (one per SIMD): reads and MFMAs of a tile are left to the
-    // compiler's schedule, the barrier closes the tile
+    // reads and MFMAs of a tile are left to the compiler's schedule, the
+    // barrier closes the tile
     if (nk > 0) issue(0);
     wait_loads();
     __syncthreads();
@@ -409,26 +422,31 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   // global reads and writes of the epilogue are contiguous 16-byte vectors.
   constexpr int PITCH = WN + 4;           // floats per staged row
   constexpr int LPR = WN / 8;             // 8-column vectors (lanes) per row in the read-back
-  static_assert((32 * LPR) % 64 == 0, "read-back passes must cover whole rows");
-  static_assert((EPI != EPI_XENT_STATS && EPI != EPI_QKNORM) || 64 % LPR == 0,
+  static_assert((SR * LPR) % 64 == 0, "read-back passes must cover whole rows");
+  static_assert((EPI != EPI_XENT_STATS && EPI != EPI_QKNORM) || (64 % LPR == 0 && SR == 32),
                 "row reductions need a row's lanes in one pass");
-  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * PITCH);
+  float* ep = reinterpret_cast<float*>(lds) + wave * (SR * PITCH);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+  for (int h = 0; h < 32 / SR; ++h) {
+    if (SR == 32 || (lrow / SR) == h) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(ep + lrow * PITCH + 32 * j + 8 * g + 4 * lhalf) =
-            make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(ep + (lrow - h * SR) * PITCH + 32 * j + 8 * g + 4 * lhalf) =
+              make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+    }
     __builtin_amdgcn_wave_barrier();
-    for (int pass = 0; pass < 32 * LPR / 64; ++pass) {
+    for (int pass = 0; pass < SR * LPR / 64; ++pass) {
       const int item = pass * 64 + lane;
-      const int row = item / LPR;
+      const int row = h * SR + item / LPR;  // row within the 32-row strip
       const int col = (item % LPR) * 8;
+      const float* er = ep + (row - h * SR) * PITCH;
       float v[8];
-      const float4 a = *reinterpret_cast<const float4*>(ep + row * PITCH + col);
-      const float4 b = *reinterpret_cast<const float4*>(ep + row * PITCH + col + 4);
+      const float4 a = *reinterpret_cast<const float4*>(er + col);
+      const float4 b = *reinterpret_cast<const float4*>(er + col + 4);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
       const int m = m0 + wm + 32 * i + row;
       const int n = n0 + wn + col;
@@ -686,7 +704,13 @@ Plan plan_mfma(const GemmDesc& d) {
   Plan pl;
   const long t256 = (long)cdiv(d.M, 256) * cdiv(d.N, 256);
   const long t160 = (long)cdiv(d.M, 256) * cdiv(d.N, 160);
-  if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM || t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
+  const long t320 = (long)cdiv(d.M, 256) * cdiv(d.N, 320);
+  // whole rounds of the 256 CUs: 256 x 320 when it fills them exactly and
+  // 256 x 256 would leave a partial round (e.g. N = 5120, M = 8192)
+  const bool r320 = d.N % 320 == 0 && t320 >= 256 && t320 % 256 == 0 && t256 % 256 != 0;
+  if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
+  else if (r320 && d.epi != EPI_F32 && !d.b_kmaj) { pl.BMv = 256; pl.BNv = 320; }
+  else if (t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else if (d.N % 160 == 0 && t160 >= 240 && t160 % 256 <= 16) { pl.BMv = 256; pl.BNv = 160; }
   else { pl.BMv = 128; pl.BNv = 128; }
   const long tiles = (long)cdiv(d.M, pl.BMv) * cdiv(d.N, pl.BNv);
@@ -725,6 +749,16 @@ hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
 template <bool AK, bool BKm, int EPI>
 hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
   if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
+  if (pl.BNv == 320) {
+    // 8 waves of 64 x 160 (k-contiguous B only: a k-major B spills here)
+    if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM || EPI == EPI_F32 || BKm) {
+      return hipErrorInvalidValue;
+    } else {
+      dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 320, 8, 4>), grid, dim3(512), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (pl.BNv == 160) {
     if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM) {
       return hipErrorInvalidValue;
