@@ -245,12 +245,15 @@ struct StageKm {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(base + off));
   }
   // fragment of tile column `row` (an m or n index): k slots 16 kk + 8 hf + 0..7
+  // (the swizzles have period 16 in the k-row, so k-step kk only adds a
+  // constant offset of 16 rows)
   static __device__ __forceinline__ bf16x8 frag(const uint4* lds, int row, int kk, int lane) {
     const int i = lane & 15;
     const int col = (row & ~15) + 4 * (i & 3);
-    const int k0 = 16 * kk + 8 * (lane >> 5) + (i >> 2);
-    const i16x4 a = tr(lds, k0, col);
-    const i16x4 b = tr(lds, k0 + 4, col);
+    const int r0 = 8 * (lane >> 5) + (i >> 2);
+    const uint4* step = lds + kk * 16 * UPR;
+    const i16x4 a = tr(step, r0, col);
+    const i16x4 b = tr(step, r0 + 4, col);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
@@ -709,7 +712,7 @@ Plan plan_mfma(const GemmDesc& d) {
   // 256 x 256 would leave a partial round (e.g. N = 5120, M = 8192)
   const bool r320 = d.N % 320 == 0 && t320 >= 256 && t320 % 256 == 0 && t256 % 256 != 0;
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
-  else if (r320 && d.epi != EPI_F32 && !d.b_kmaj) { pl.BMv = 256; pl.BNv = 320; }
+  else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
   else if (t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else if (d.N % 160 == 0 && t160 >= 240 && t160 % 256 <= 16) { pl.BMv = 256; pl.BNv = 160; }
   else { pl.BMv = 128; pl.BNv = 128; }
@@ -750,8 +753,8 @@ template <bool AK, bool BKm, int EPI>
 hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
   if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
   if (pl.BNv == 320) {
-    // 8 waves of 64 x 160 (k-contiguous B only: a k-major B spills here)
-    if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM || EPI == EPI_F32 || BKm) {
+    // 8 waves of 64 x 160
+    if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM || EPI == EPI_F32) {
       return hipErrorInvalidValue;
     } else {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
