@@ -26,15 +26,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "hbm_traffic_d20_block_fwd_bwd.md")
 CSRC = os.path.join(HERE, "decoder_only_gpt_bf16_amd", "csrc")
 
-# call site -> (kernel as named in the counter summary, its source files);
+# call site -> (kernels as named in the counter summary, their source files);
 # sites that share a GEMM instance with others have no entry
 SITE_KERNEL = {
-    "attn_fwd": ("attn_fwd_mfma<128>", "attention"), "attn_bwd_dkdv": ("attn_bwd_dkdv_mfma<128>", "attention"),
-    "attn_bwd_dq": ("attn_bwd_dq_mfma<128>", "attention"), "qk_rope_norm": ("qk_fwd_k<...>", "attention"),
-    "qk_bwd": ("qk_bwd_k<...>", "attention"), "attn_delta": ("delta_k<...>", "attention"),
-    "qkv_gemm": ("gemm_mfma<false, false, 0, 256, 256>", "gemm"),
-    "fc_gemm_gelu": ("gemm_mfma<false, false, 1, 256, 256>", "gemm"),
-    "proj_dgrad_gelu": ("gemm_mfma<false, true, 2, 256, 256>", "gemm"),
+    "attn_fwd": (["attn_fwd_mfma<128>"], "attention"),
+    "attn_bwd_dkdv": (["attn_bwd_dkdv_mfma<128>"], "attention"),
+    "attn_bwd_dq": (["attn_bwd_dq_mfma<128>"], "attention"),
+    "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 4>"], "gemm"),
+    "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4>"], "gemm"),
+    "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4>"], "gemm"),
+    "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2>", "streamk_fixup<256, 256>"], "gemm"),
 }
 SOURCES = {"attention": ["attention.hip", "common.h", "kernels.h"], "gemm": ["gemm.hip", "common.h", "kernels.h"]}
 
@@ -93,14 +94,17 @@ def measured_traffic(site):
     the counters were taken."""
     if site not in SITE_KERNEL or not os.path.exists(TRAFFIC_PROFILE):
         return None
-    kernel, fam = SITE_KERNEL[site]
+    kernels, fam = SITE_KERNEL[site]
     want = source_hash(fam)
+    found = {}
     with open(TRAFFIC_PROFILE) as fh:
         for line in fh:
             cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
-            if len(cells) == 6 and cells[0] == kernel:
-                return int(cells[4]) if cells[5] == want else None
-    return None
+            if len(cells) == 6 and cells[0] in kernels:
+                if cells[5] != want:
+                    return None
+                found[cells[0]] = int(cells[4])
+    return sum(found.values()) if len(found) == len(kernels) else None
 
 
 def cpu_baseline(w, min_s=12.0):
