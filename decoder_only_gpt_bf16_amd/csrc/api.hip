@@ -130,6 +130,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // ------------------------------------------------------------ block layouts
 struct Saved {
+  float2* cs;                            // RoPE (cos, sin) table [T][D/2], written by the forward
   void *a1, *qkv, *o, *x1, *a2, *u, *g;  // u holds GELU'(fc output), g = GELU(fc output)
   float *stats1, *stats2, *qkr, *lse;
 };
@@ -137,6 +138,7 @@ struct Saved {
 Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   Saved s{};
   const size_t N = d.N, C = d.C, es = d.es;
+  s.cs = cfg->rope ? a.take_n<float2>((size_t)d.T * (d.D / 2)) : nullptr;
   s.a1 = a.take(N * C * es);
   s.stats1 = a.take_n<float>(2 * N);
   s.qkv = a.take(N * 3 * C * es);
@@ -152,7 +154,6 @@ Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
 }
 
 struct BwdWs {
-  float2* cs;
   void *du, *da, *dx1, *dO, *dqkv;
   float *delta, *colpart, *colsum, *split;
 };
@@ -207,7 +208,6 @@ size_t split_need(const Dims& d) {
 BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   BwdWs w{};
   const size_t N = d.N, C = d.C, es = d.es;
-  w.cs = cfg->rope ? a.take_n<float2>((size_t)d.T * (d.D / 2)) : nullptr;
   w.du = a.take(N * 4 * C * es);
   w.da = a.take(N * C * es);
   w.dx1 = a.take(N * C * es);
@@ -222,7 +222,6 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
 
 size_t fwd_ws_bytes(const Dims& d, const gpt_config* cfg, bool inference) {
   Arena a(nullptr);
-  if (cfg->rope) a.take_n<float2>((size_t)d.T * (d.D / 2));
   if (inference) saved_layout(d, cfg, a);
   return a.used();
 }
@@ -397,10 +396,9 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   if (need && (!ws || ws_bytes < need))
     return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Arena wa(ws);
-  float2* cs = cfg->rope ? wa.take_n<float2>((size_t)T * (d.D / 2)) : nullptr;
-  Arena sa(saved ? saved : wa.take(0));  // inference: intermediates follow the table
+  Arena sa(saved ? saved : ws);  // inference: intermediates live in the workspace
   Saved sv = saved_layout(d, cfg, sa);
+  float2* cs = sv.cs;
   const int C = d.C, ty = d.dtype, kind = cfg->norm;
 
   if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, cs, s));
@@ -418,7 +416,7 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   RUN("qkv_gemm", launch_gemm(g, ty, nullptr, s));
   if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
-  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, sv.qkv, sv.o, sv.lse, s));
+  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, sv.qkv, sv.o, sv.lse, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
   g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
   RUN("out_gemm", launch_gemm(g, ty, nullptr, s));
@@ -461,7 +459,6 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   const int nblk = norm_bwd_blocks(N);
   const bool ln = kind == GPT_NORM_LAYERNORM;
 
-  if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, b.cs, s));
   // MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
   GemmDesc g = lin_dgrad(d, dy, C, w->w_proj, 4 * C, EPI_GELU_BWD);
   g.out = b.du; g.ldc = 4 * C; g.aux = sv.u; g.ldaux = 4 * C;
@@ -491,7 +488,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
   if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
   // attention
-  const QkBwd qk{cfg->rope, cfg->qk_norm, N, b.cs, sv.qkr};
+  const QkBwd qk{cfg->rope, cfg->qk_norm, N, sv.cs, sv.qkr};
   if (attn_mfma_supported(ty, d.D)) {
     // dQ pass first (it also forms delta); QK-norm / RoPE backward in both stores
     RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
@@ -501,7 +498,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
     RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
     if (cfg->rope || cfg->qk_norm)
-      RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, b.cs, sv.qkv, sv.qkr, b.dqkv, s));
+      RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, sv.cs, sv.qkv, sv.qkr, b.dqkv, s));
   }
   // fused QKV projection
   g = lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);

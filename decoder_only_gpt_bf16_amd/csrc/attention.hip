@@ -134,6 +134,18 @@ struct RowTile {
 
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Sum / max of v over the lane pair (l, l ^ 32), returned to both lanes.
+// v_permlane32_swap exchanges the upper half of one copy with the lower half
+// of the other, so each lane then holds both values (no LDS round trip).
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A operand from tile rows: row r, k-step ks (columns 16 ks + 8 hf .. + 7).
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const uint4* s, int r, int ks, int hf) {
@@ -176,10 +188,14 @@ __device__ __forceinline__ void attn_block(int T, int H, int& rank, int& h, int&
   h = bh % H;
   b = bh / H;
 }
-template <int D>
+// FIXED: the scores are known to lie below shift_log2 (in log2 units), so
+// every exponent uses that constant shift instead of a running maximum:
+// softmax is shift-invariant, and with QK-norm |q . k| <= |q| |k| <= D bounds
+// the scaled score by sqrt(D), so exp2 neither overflows nor underflows.
+template <int D, bool FIXED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                         bf16* __restrict__ o, float* __restrict__ lse,
-                                                        float scale_log2) {
+                                                        float scale_log2, float shift_log2) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
@@ -211,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = FIXED ? shift_log2 : -INFINITY, l_run = 0.0f;
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
@@ -271,10 +287,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       };
       const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
       float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const bool dead = (m_new == -INFINITY);
-      const float msub = dead ? 0.0f : m_new;
+      float m_new = m_run, msub = m_run;
+      bool dead = false;
+      if constexpr (!FIXED) {
+        mx = pair32_max(mx);
+        m_new = fmaxf(m_run, mx * scale_log2);
+        dead = (m_new == -INFINITY);
+        msub = dead ? 0.0f : m_new;
+      }
       float rs = 0.0f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
@@ -284,16 +304,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
           p[jt][r] = e;
           rs += e;
         }
-      rs += __shfl_xor(rs, 32, 64);
+      rs = pair32_sum(rs);
       // rescale the running sums only when some row's maximum grew (a
       // factor of exactly 1 otherwise)
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        const float corr = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= corr;
+      if constexpr (!FIXED) {
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+          const float corr = dead ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= corr;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+            for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+        }
       }
       l_run += rs;
       m_run = m_new;
@@ -359,7 +381,7 @@ __device__ __forceinline__ void qk_row_bwd(float (&g)[D / 32][16], const bf16* _
 #pragma unroll
         for (int e = 0; e < 4; ++e) part = fmaf(g[dt][4 * q + e], y[dt][4 * q + e], part);
       }
-    part += __shfl_xor(part, 32, 64);
+    part = pair32_sum(part);
     const float m = part / D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -622,7 +644,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[s2][e], part);
     }
-    Dl = part + __shfl_xor(part, 32, 64);
+    Dl = pair32_sum(part);
     if (qi < T && hf == 0) delta[row_lse] = Dl;
   }
   f32x16 dq[DT];
@@ -807,15 +829,24 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simt(int TT, int H, const T*
 }
 
 // ----------------------------------------------------- RoPE / QK-norm, delta
-__global__ void rope_table_k(int T, int D, double base, float2* cs) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+// cs[t][i] = (cos, sin)(t theta_i), theta_i = base^(-2 i / D).  The block's
+// frequencies are computed once in double; each angle t theta_i is formed
+// and reduced to [-pi, pi] in double, so the float sincos that follows is
+// accurate to a few ulp for any position.
+__global__ __launch_bounds__(256) void rope_table_k(int T, int D, double base, float2* cs) {
+  __shared__ double th[256];
   const int half = D / 2;
+  if ((int)threadIdx.x < half) th[threadIdx.x] = pow(base, -2.0 * threadIdx.x / D);
+  __syncthreads();
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * half) return;
   const int t = idx / half, i = idx % half;
-  const double theta = pow(base, -2.0 * i / D);
-  double sn, c;
-  sincos((double)t * theta, &sn, &c);
-  cs[idx] = make_float2((float)c, (float)sn);
+  constexpr double TWO_PI = 6.283185307179586476925286766559;
+  const double a = (double)t * th[i];
+  const float r = (float)(a - TWO_PI * rint(a * (1.0 / TWO_PI)));
+  float sn, c;
+  sincosf(r, &sn, &c);
+  cs[idx] = make_float2(c, sn);
 }
 
 // One wavefront per (row, head, q|k); lane i < D/2 handles pair (i, i + D/2).
@@ -976,15 +1007,22 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qkv, void* o, float* lse,
-                           hipStream_t s) {
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, const void* qkv, void* o,
+                           float* lse, hipStream_t s) {
   if (attn_mfma_supported(dtype, D)) {
     const float scale_log2 = LOG2E / sqrtf((float)D);
+    // with QK-norm |q|, |k| <= sqrt(D) (up to bf16 rounding), so a scaled
+    // score is at most sqrt(D); the shift adds 3% for the rounding
+    const float shift_log2 = 1.03f * sqrtf((float)D) * LOG2E;
     dim3 grid(cdiv(T, 128) * H * B);
-    if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, T, H, (const bf16*)qkv, (bf16*)o, lse, scale_log2);
-    else
-      hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, T, H, (const bf16*)qkv, (bf16*)o, lse, scale_log2);
+#define AF(DD, FX) hipLaunchKernelGGL((attn_fwd_mfma<DD, FX>), grid, dim3(256), 0, s, T, H, (const bf16*)qkv, \
+                                      (bf16*)o, lse, scale_log2, shift_log2)
+    if (D == 128) {
+      if (qk_norm) AF(128, true); else AF(128, false);
+    } else {
+      if (qk_norm) AF(64, true); else AF(64, false);
+    }
+#undef AF
     return hipGetLastError();
   }
   if (dtype == 1) return simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, s);

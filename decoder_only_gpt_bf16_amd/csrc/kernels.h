@@ -130,7 +130,9 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
                          const float2* cs, const void* qkv, const float* rstd, void* dqkv,
                          hipStream_t s);
 // Causal attention forward: q, k, v inside qkv [N, 3C]; o [N, C]; lse fp32 [B, H, T].
-hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, const void* qkv, void* o,
+// qk_norm != 0 promises RMS-normalised q and k (|q|, |k| <= sqrt(D)), which
+// lets the softmax use a fixed shift instead of a running maximum.
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, const void* qkv, void* o,
                            float* lse, hipStream_t s);
 // delta[b, h, t] = sum_d dO * O (fp32 [B, H, T]).
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO,

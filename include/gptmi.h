@@ -113,8 +113,9 @@ size_t gpt_workspace_bytes(const gpt_config* cfg, int B, int T);
  *   x     [B*T, C] input (dtype); the caller keeps it alive until the
  *         matching gpt_block_bwd.
  *   y     [B*T, C] output (dtype).
- *   saved gpt_block_saved_bytes() bytes, filled for the backward; NULL runs
- *         inference only (intermediates then live in the workspace).
+ *   saved gpt_block_saved_bytes() bytes, filled for the backward (with the
+ *         RoPE table it reads too); NULL runs inference only (intermediates
+ *         then live in the workspace, which is otherwise not touched).
  * Errors: INVALID (null pointer, B/T <= 0, T > block_size, n_embd % n_head,
  * odd head_dim with rope), UNSUPPORTED (bf16 with head_dim not in {64,128}
  * or C % 8 != 0), WORKSPACE, HIP. */

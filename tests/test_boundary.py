@@ -66,7 +66,7 @@ def test_block_fwd_validation(L):
     assert b"block_size" in L.gpt_last_error()
     assert _fwd(L, c, 1, 16, w, x=None) == B.GPT_ERR_INVALID
     assert _fwd(L, c, 1, 16, w, x=FAKE + 4) == B.GPT_ERR_INVALID  # misaligned
-    assert _fwd(L, c, 1, 16, w, nbytes=1) == B.GPT_ERR_WORKSPACE
+    assert _fwd(L, c, 1, 16, w, saved=None, nbytes=1) == B.GPT_ERR_WORKSPACE  # inference keeps intermediates there
     bad = _weights(cfg)
     bad.w_fc = None
     assert _fwd(L, c, 1, 16, bad) == B.GPT_ERR_INVALID
