@@ -132,7 +132,12 @@ struct RowTile {
   }
 };
 
-__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits on the vector-memory counter through the s_waitcnt builtin rather
+// than inline asm, so that the compiler's own wait insertion sees them and
+// adds no second, stricter wait before the LDS reads of a landed tile.
+// Encoding (gfx9): vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at
+// their maxima (no wait).
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Sum / max of v over the lane pair (l, l ^ 32), returned to both lanes.
 // v_permlane32_swap exchanges the upper half of one copy with the lower half
@@ -236,8 +241,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
   wait_lds_loads();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
+  // the loop is unrolled by two so that every LDS buffer index is a
+  // compile-time constant: the compiler can then tell the next tile's
+  // asynchronous copies from this tile's reads and inserts no wait between
+  auto tile = [&](int t, auto curc) {
+    constexpr int cur = decltype(curc)::value;
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
@@ -337,6 +345,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
     }
     wait_lds_loads();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (qi < T) {
@@ -659,8 +671,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
   RowTile<D>::direct(sV[0], rV, ld, 0, T);
   wait_lds_loads();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
+  // the loop is unrolled by two so that every LDS buffer index is a
+  // compile-time constant: the compiler can then tell the next tile's
+  // asynchronous copies from this tile's reads and inserts no wait between
+  auto tile = [&](int t, auto curc) {
+    constexpr int cur = decltype(curc)::value;
     const bool more = t + 1 < ntiles;
     const int kv0 = t * 64;
     if (more) {
@@ -710,6 +725,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
     }
     wait_lds_loads();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
   if (qi < T) {
     bf16* qrow = dqkv + ((long)b * T + qi) * ld + h * D;
