@@ -117,6 +117,23 @@ struct RowTile {
   // i.e. row P / KU, slot P % KU, which holds logical unit slot ^ f(row);
   // lane L's 16 bytes land at the wave-uniform base + 16 L, and rows >= T
   // (out-of-range offsets) arrive as zeros.
+  // the same copy spread over NW waves (NW * 64 threads)
+  template <int NW>
+  static __device__ __forceinline__ void direct_by(uint4* s, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
+    static_assert((64 * KU) % (64 * NW) == 0, "whole copies per wave");
+    constexpr int N = 64 * KU / (64 * NW);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int P = (NW * i + w) * 64 + lane;
+      const int row = P / KU;
+      const int u = (P % KU) ^ swz<D>(row);
+      const int r = r0 + row;
+      const uint32_t off = r < T ? (uint32_t)(((long)r * ld + 8 * u) * 2) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(s + (NW * i + w) * 64),
+                                               16, off, 0, 0, 0);
+    }
+  }
   static __device__ __forceinline__ void direct(uint4* s, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int T) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -138,6 +155,17 @@ struct RowTile {
 // Encoding (gfx9): vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at
 // their maxima (no wait).
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier for LDS data: this wave's LDS accesses complete, then
+// s_barrier.  Global -> LDS copies in flight stay in flight (__syncthreads
+// would also wait for those); the "memory" clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// all but the N (< 16) most recently issued vector-memory operations have retired
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Sum / max of v over the lane pair (l, l ^ 32), returned to both lanes.
 // v_permlane32_swap exchanges the upper half of one copy with the lower half
@@ -420,17 +448,49 @@ __device__ __forceinline__ void qk_row_bwd(float (&g)[D / 32][16], const bf16* _
 }
 
 // ------------------------------------------------------ backward dK, dV (MFMA)
+// A workgroup owns 128 keys of one (batch, head) and runs 8 waves as 4
+// pairs; a pair owns 32 keys (one lane per key and lane half) and splits the
+// work of every 32-query half tile n:
+//   wave a (waves 0-3): S(n) = Q K^T, then P(n) = exp(S - lse) and
+//       dS(n) = P (dP - delta), then dV^T += dO^T P;
+//   wave b (waves 4-7): dP(n) = dO V^T, then dK^T += Q^T dS.
+// dP goes b -> a and dS goes a -> b through LDS.  b runs one half ahead on
+// dP and a one half ahead on S, so the two waves of a pair (which share a
+// SIMD) alternate: while a works through the exponentials, b's MFMAs run.
+// Each wave holds one 32-key accumulator set (dV or dK) and one set of key
+// fragments (K or V), so two waves fit per SIMD.  Periods, separated by
+// workgroup barriers (n = 2t + it for query tile t):
+//   A(n): a: P, dS of half n, dV += ...;   b: dP(n + 1)
+//   B(n): a: S(n + 1);                     b: dK += dS(n) ...
+// Query tiles (Q, dO, log-sum-exp, delta) stream global -> LDS through three
+// buffers: tile t + 2 is issued at A(2t) into the buffer of tile t - 1, and
+// tile t + 1 must have landed before A(2t + 1).  The tile loop is unrolled by
+// three so that every buffer index is a compile-time constant (the compiler
+// then inserts no wait behind the copies in flight).
 template <int D>
-__global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                              const bf16* __restrict__ dO,
                                                              const float* __restrict__ lse,
                                                              const float* __restrict__ delta,
                                                              bf16* __restrict__ dqkv, float scale_log2,
                                                              float scale, QkBwd qk) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
-  __shared__ uint4 sQ[2][64 * KU];
-  __shared__ uint4 sdO[2][64 * KU];
-  __shared__ float sL[2][64], sDl[2][64];
+  constexpr int NCP = 2 * (64 * KU / 512);  // tile copies per wave (Q and dO)
+  __shared__ uint4 sQ[3][64 * KU];
+  __shared__ uint4 sdO[3][64 * KU];
+  // log-sum-exp and delta per buffer as separate arrays (each a distinct
+  // object to the compiler's alias analysis)
+  __shared__ float sL0[64], sL1[64], sL2[64], sD0[64], sD1[64], sD2[64];
+  __shared__ float4 xdP[4][2][4][64];  // [pair][half parity][register quad][lane]
+  __shared__ uint4 xdS[4][2][2][64];   // [pair][half parity][16-key step][lane]
+  auto sLb = [&](auto bc) __attribute__((always_inline)) -> float* {
+    constexpr int bf = decltype(bc)::value;
+    return bf == 0 ? sL0 : bf == 1 ? sL1 : sL2;
+  };
+  auto sDb = [&](auto bc) __attribute__((always_inline)) -> float* {
+    constexpr int bf = decltype(bc)::value;
+    return bf == 0 ? sD0 : bf == 1 ? sD1 : sD2;
+  };
   int rank, h, b;
   attn_block(T, H, rank, h, b);
   const int C = H * D;
@@ -442,165 +502,211 @@ __global__ __launch_bounds__(256, (D >= 128 ? 1 : 2)) void attn_bwd_dkdv_mfma(in
   const float* Lg = lse + ((long)b * H + h) * T;
   const float* Dg = delta + ((long)b * H + h) * T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pair = wave & 3;
+  const bool is_b = wave >= 4;
   const int li = lane & 31, hf = lane >> 5;
   const int k0 = rank * 128;
-  const int kw = k0 + 32 * wave;
+  const int kw = k0 + 32 * pair;
   const int kj = kw + li;
 
   const __amdgpu_buffer_rsrc_t rQ = slice_rsrc(Qg, T, ld, D);
-  const __amdgpu_buffer_rsrc_t rK = slice_rsrc(Kg, T, ld, D);
-  const __amdgpu_buffer_rsrc_t rV = slice_rsrc(Vg, T, ld, D);
   const __amdgpu_buffer_rsrc_t rO = slice_rsrc(dOg, T, C, D);
-  bf16x8 kf[KS], vf[KS];
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(Lg, (long)T * 4);
+  const __amdgpu_buffer_rsrc_t rD = make_rsrc(Dg, (long)T * 4);
+  // the pair's key row fragments: K for wave a (S), V for wave b (dP)
+  bf16x8 kv[KS];
+  {
+    const __amdgpu_buffer_rsrc_t rKV = slice_rsrc(is_b ? Vg : Kg, T, ld, D);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint32_t off = kj < T ? (uint32_t)(((long)kj * ld + 16 * s + 8 * hf) * 2) : OOB;
-    kf[s] = u4_bf8(bload(rK, off));
-    vf[s] = u4_bf8(bload(rV, off));
+    for (int s = 0; s < KS; ++s)
+      kv[s] = u4_bf8(bload(rKV, kj < T ? (uint32_t)(((long)kj * ld + 16 * s + 8 * hf) * 2) : OOB));
   }
-  f32x16 dk[DT], dv[DT];
+  f32x16 acc[DT];  // dV^T (wave a) or dK^T (wave b) of the pair's keys
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[dt][r] = 0.0f; dv[dt][r] = 0.0f; }
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
 
   const int t_begin = k0 / 64;
   const int t_end = (T + 63) / 64;
-  // Q and dO tiles stream global -> LDS asynchronously; the tile's log-sum-exp
-  // and delta values are prefetched into registers one tile ahead
-  float lpre = 0.0f, dpre = 0.0f;
-  auto stage_issue = [&](int t, int buf) {
+  // Q and dO tiles by all 8 waves; every wave also copies the tile's 64
+  // log-sum-exp and delta values (4 bytes a lane, the same bytes to the same
+  // place), so that all waves issue the same number of copies and the wait
+  // below needs no branch; rows at or past T read as zeros
+  auto stage_issue = [&](int t, auto bc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bc)::value;
     const int qt0 = t * 64;
-    RowTile<D>::direct(sQ[buf], rQ, ld, qt0, T);
-    RowTile<D>::direct(sdO[buf], rO, C, qt0, T);
-    if (threadIdx.x < 64) {
-      const int q = qt0 + threadIdx.x;
-      lpre = q < T ? Lg[q] * LOG2E : 0.0f;
-      dpre = q < T ? Dg[q] : 0.0f;
-    }
+    RowTile<D>::template direct_by<8>(sQ[bf], rQ, ld, qt0, T);
+    RowTile<D>::template direct_by<8>(sdO[bf], rO, C, qt0, T);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)sLb(bc), 4,
+                                             (uint32_t)((qt0 + lane) * 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (__attribute__((address_space(3))) void*)sDb(bc), 4,
+                                             (uint32_t)((qt0 + lane) * 4), 0, 0, 0);
   };
-  auto stage_finish = [&](int buf) {
-    if (threadIdx.x < 64) {
-      sL[buf][threadIdx.x] = lpre;
-      sDl[buf][threadIdx.x] = dpre;
-    }
-    wait_lds_loads();
+  // every copy but the most recent tile's has landed
+  auto wait_but_tile = [&]() __attribute__((always_inline)) { wait_loads_but<NCP + 2>(); };
+
+  f32x16 S;  // wave a: scores of the next half, carried from B(n - 1) to A(n)
+  // S or dP of half it of the tile in buffer bf (rows of Q or dO times the
+  // pair's K or V fragments)
+  auto scores = [&](f32x16& out, const uint4* src, int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(src, 32 * it + li, s, hf), kv[s], out, 0, 0, 0);
   };
-  if (t_begin < t_end) {
-    stage_issue(t_begin, 0);
-    stage_finish(0);
-  }
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    const int qt0 = t * 64;
-    if (more) stage_issue(t + 1, cur ^ 1);
-    {
-      // the 64-query tile is processed as two 32-query halves: S = Q K^T and
-      // dP = dO V^T for the half, P and dS, then dV^T += dO^T P and
-      // dK^T += Q^T dS over it; only one half's scores are live at a time.
-      // Halves whose queries all precede the wave's keys are not skipped but
-      // masked to P = 0: the accumulators then follow one straight path (no
-      // register copies at the joins), and with one wave per SIMD the other
-      // waves of the block would wait at the barrier anyway
+  auto phase_dP = [&](auto bc, int it, int xb) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bc)::value;
+    f32x16 dP;
+    scores(dP, sdO[bf], it);
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        // LLVM's igrouplp strategy 0 interleaves the LDS reads with the
-        // MFMAs of the half (measured 7% faster for this one-wave-per-SIMD
-        // kernel; no change for the forward and dQ kernels)
-        __builtin_amdgcn_iglp_opt(0);
-        const int q0h = qt0 + 32 * it;
-        f32x16 S, dP;
+    for (int q = 0; q < 4; ++q)
+      xdP[pair][xb][q][lane] = make_float4(dP[4 * q], dP[4 * q + 1], dP[4 * q + 2], dP[4 * q + 3]);
+  };
+  // wave a: P and dS of half it (tile t, buffer bf), dS to the partner, then
+  // dV^T += dO^T P
+  auto phase_P = [&](auto bc, int t, int it) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bc)::value;
+    const int q0h = t * 64 + 32 * it;
+    uint32_t pw[8], dw[8];
+    auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { S[r] = 0.0f; dP[r] = 0.0f; }
+      for (int g = 0; g < 4; ++g) {
+        const int il = 32 * it + 8 * g + 4 * hf;
+        const float4 L4 = *reinterpret_cast<const float4*>(sLb(bc) + il);
+        const float4 D4 = *reinterpret_cast<const float4*>(sDb(bc) + il);
+        const float4 P4 = xdP[pair][it][g][lane];
+        const float Ls[4] = {L4.x * LOG2E, L4.y * LOG2E, L4.z * LOG2E, L4.w * LOG2E};
+        const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+        const float dPs[4] = {P4.x, P4.y, P4.z, P4.w};
+        float pv[4], dv4[4];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sQ[cur], 32 * it + li, s, hf), kf[s], S, 0, 0, 0);
-          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(sdO[cur], 32 * it + li, s, hf), vf[s], dP, 0, 0, 0);
-        }
-        // P and dS go straight to packed bf16 B operands (k-slot order of
-        // pack_slots: registers 8 kh + 0..7)
-        uint32_t pw[8], dw[8];
-        auto probs = [&](auto masked) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int il = 32 * it + 8 * g + 4 * hf;
-            const float4 L4 = *reinterpret_cast<const float4*>(&sL[cur][il]);
-            const float4 D4 = *reinterpret_cast<const float4*>(&sDl[cur][il]);
-            const float Ls[4] = {L4.x, L4.y, L4.z, L4.w};
-            const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
-            float pv[4], dv4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float x = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, -Ls[e]));
-              if constexpr (decltype(masked)::value) {
-                const int qi = qt0 + il + e;
-                if (qi < kj || qi >= T || kj >= T) x = 0.0f;
-              }
-              pv[e] = x;
-              dv4[e] = x * (dP[r] - Ds[e]);
-            }
-            pw[2 * g] = pack2(pv[0], pv[1]);
-            pw[2 * g + 1] = pack2(pv[2], pv[3]);
-            dw[2 * g] = pack2(dv4[0], dv4[1]);
-            dw[2 * g + 1] = pack2(dv4[2], dv4[3]);
+        for (int e = 0; e < 4; ++e) {
+          float x = __builtin_amdgcn_exp2f(fmaf(S[4 * g + e], scale_log2, -Ls[e]));
+          if constexpr (decltype(masked)::value) {
+            const int qi = q0h + 8 * g + 4 * hf + e;
+            if (qi < kj || qi >= T || kj >= T) x = 0.0f;
           }
-        };
-        if ((q0h < kw + 31) || (q0h + 32 > T) || (kw + 32 > T)) probs(std::true_type{});
-        else probs(std::false_type{});
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const bf16x8 pb = u4_bf8(make_uint4(pw[4 * kh], pw[4 * kh + 1], pw[4 * kh + 2], pw[4 * kh + 3]));
-          const bf16x8 db = u4_bf8(make_uint4(dw[4 * kh], dw[4 * kh + 1], dw[4 * kh + 2], dw[4 * kh + 3]));
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sdO[cur], dt, 2 * it + kh, lane), pb, dv[dt],
-                                                             0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sQ[cur], dt, 2 * it + kh, lane), db, dk[dt],
-                                                             0, 0, 0);
-          }
+          pv[e] = x;
+          dv4[e] = x * (dPs[e] - Ds[e]);
         }
+        pw[2 * g] = pack2(pv[0], pv[1]);
+        pw[2 * g + 1] = pack2(pv[2], pv[3]);
+        dw[2 * g] = pack2(dv4[0], dv4[1]);
+        dw[2 * g + 1] = pack2(dv4[2], dv4[3]);
       }
+    };
+    if ((q0h < kw + 31) || (q0h + 32 > T) || (kw + 32 > T)) probs(std::true_type{});
+    else probs(std::false_type{});
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+      xdS[pair][it][kh][lane] = make_uint4(dw[4 * kh], dw[4 * kh + 1], dw[4 * kh + 2], dw[4 * kh + 3]);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 pb = u4_bf8(make_uint4(pw[4 * kh], pw[4 * kh + 1], pw[4 * kh + 2], pw[4 * kh + 3]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sdO[bf], dt, 2 * it + kh, lane), pb, acc[dt],
+                                                          0, 0, 0);
     }
-    if (more) stage_finish(cur ^ 1);
-    __syncthreads();
+  };
+  // wave b: dK^T += Q^T dS for half it (dS from the partner)
+  auto phase_dK = [&](auto bc, int it) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bc)::value;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 db = u4_bf8(xdS[pair][it][kh][lane]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(sQ[bf], dt, 2 * it + kh, lane), db, acc[dt],
+                                                          0, 0, 0);
+    }
+  };
+
+  // tile t in buffer c (= (t - t_begin) % 3); tile t + 1 in c1, t + 2 in c2.
+  // Nothing inside depends on whether tiles t + 1, t + 2 exist: copies past
+  // the last tile read as zeros, and the work on them (S, dP of a half past
+  // the end) is dropped, so the waits the compiler derives need no merging
+  // of paths.
+  auto tile = [&](int t, auto cc) __attribute__((always_inline)) {
+    constexpr int c = decltype(cc)::value;
+    constexpr int c1 = (c + 1) % 3, c2 = (c + 2) % 3;
+    using C0 = std::integral_constant<int, c>;
+    using C1 = std::integral_constant<int, c1>;
+    using C2 = std::integral_constant<int, c2>;
+    // A(2t)
+    stage_issue(t + 2, C2{});
+    if (!is_b) phase_P(C0{}, t, 0);
+    else phase_dP(C0{}, 1, 1);
+    lds_barrier();
+    // B(2t)
+    if (!is_b) scores(S, sQ[c], 1);
+    else phase_dK(C0{}, 0);
+    wait_but_tile();
+    lds_barrier();  // tile t + 1 has landed
+    // A(2t + 1)
+    if (!is_b) phase_P(C0{}, t, 1);
+    else phase_dP(C1{}, 0, 0);
+    lds_barrier();
+    // B(2t + 1)
+    if (!is_b) scores(S, sQ[c1], 0);
+    else phase_dK(C0{}, 1);
+    lds_barrier();
+  };
+
+  stage_issue(t_begin, std::integral_constant<int, 0>{});
+  stage_issue(t_begin + 1, std::integral_constant<int, 1>{});
+  wait_but_tile();
+  lds_barrier();
+  // before A(0): b forms dP(0), a forms S(0)
+  if (is_b) phase_dP(std::integral_constant<int, 0>{}, 0, 0);
+  else scores(S, sQ[0], 0);
+  lds_barrier();
+  for (int t = t_begin; t < t_end; t += 3) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_end) tile(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < t_end) tile(t + 2, std::integral_constant<int, 2>{});
   }
+  wait_lds_loads();  // the copies issued past the last tile
+
   if (kj < T) {
-    bf16* krow = dqkv + ((long)b * T + kj) * ld + C + h * D;
-    bf16* vrow = krow + C;
+    if (!is_b) {
+      bf16* vrow = dqkv + ((long)b * T + kj) * ld + 2 * C + h * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hf;
-        uint2 u;
-        u.x = pack2(dv[dt][4 * g], dv[dt][4 * g + 1]);
-        u.y = pack2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
-        *reinterpret_cast<uint2*>(vrow + d) = u;
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * hf;
+          uint2 u;
+          u.x = pack2(acc[dt][4 * g], acc[dt][4 * g + 1]);
+          u.y = pack2(acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+          *reinterpret_cast<uint2*>(vrow + d) = u;
+        }
+    } else {
+      bf16* krow = dqkv + ((long)b * T + kj) * ld + C + h * D;
+      float gk[DT][16];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gk[dt][r] = acc[dt][r] * scale;
+      if (qk.rope | qk.qk_norm) {
+        const long n = (long)b * T + kj;
+        const float r_inv = qk.qk_norm ? qk.rstd[(long)qk.N * H + n * H + h] : 1.0f;
+        qk_row_bwd<D>(gk, Kg + (long)kj * ld, r_inv, qk.rope ? qk.cs + (long)kj * (D / 2) : nullptr, hf, qk.rope,
+                       qk.qk_norm);
       }
-    float gk[DT][16];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) gk[dt][r] = dk[dt][r] * scale;
-    if (qk.rope | qk.qk_norm) {
-      const long n = (long)b * T + kj;
-      const float r_inv = qk.qk_norm ? qk.rstd[(long)qk.N * H + n * H + h] : 1.0f;
-      qk_row_bwd<D>(gk, Kg + (long)kj * ld, r_inv, qk.rope ? qk.cs + (long)kj * (D / 2) : nullptr, hf, qk.rope,
-                     qk.qk_norm);
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * hf;
+          uint2 u;
+          u.x = pack2(gk[dt][4 * g], gk[dt][4 * g + 1]);
+          u.y = pack2(gk[dt][4 * g + 2], gk[dt][4 * g + 3]);
+          *reinterpret_cast<uint2*>(krow + d) = u;
+        }
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hf;
-        uint2 u;
-        u.x = pack2(gk[dt][4 * g], gk[dt][4 * g + 1]);
-        u.y = pack2(gk[dt][4 * g + 2], gk[dt][4 * g + 3]);
-        *reinterpret_cast<uint2*>(krow + d) = u;
-      }
   }
 }
 
@@ -1066,10 +1172,10 @@ hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const voi
     const float scale_log2 = LOG2E * scale;
     dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
-      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(512), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
                          delta, (bf16*)dqkv, scale_log2, scale, qk);
     else
-      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
+      hipLaunchKernelGGL(attn_bwd_dkdv_mfma<64>, g, dim3(512), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
                          delta, (bf16*)dqkv, scale_log2, scale, qk);
     return hipGetLastError();
   }
