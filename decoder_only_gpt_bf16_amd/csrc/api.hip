@@ -156,6 +156,7 @@ Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
 struct BwdWs {
   void *du, *da, *dx1, *dO, *dqkv;
   float *delta, *colpart, *colsum, *split;
+  void *wt_fc, *wt_o, *wt_qkv;  // bf16: transposed weights for the input gradients
 };
 
 GemmDesc gemm0() {
@@ -177,6 +178,15 @@ GemmDesc lin_dgrad(const Dims& d, const void* dY, int Out, const void* W, int In
   GemmDesc g = gemm0();
   g.A = dY; g.lda = Out; g.a_kmaj = false;
   g.B = W; g.ldb = In; g.b_kmaj = true;
+  g.M = d.N; g.N = In; g.K = Out; g.epi = epi;
+  return g;
+}
+// the same from a transposed copy WT[In, Out] of the weight: both operands
+// then have k contiguous
+GemmDesc lin_dgrad_t(const Dims& d, const void* dY, int Out, const void* WT, int In, int epi) {
+  GemmDesc g = gemm0();
+  g.A = dY; g.lda = Out; g.a_kmaj = false;
+  g.B = WT; g.ldb = Out; g.b_kmaj = false;
   g.M = d.N; g.N = In; g.K = Out; g.epi = epi;
   return g;
 }
@@ -217,6 +227,11 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   w.colpart = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
   w.colsum = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, 4 * C)));
   w.split = static_cast<float*>(a.take(split_need(d)));
+  if (d.dtype == GPT_DTYPE_BF16) {
+    w.wt_fc = a.take(4 * C * C * es);
+    w.wt_o = a.take(C * C * es);
+    w.wt_qkv = a.take(3 * C * C * es);
+  }
   return w;
 }
 
@@ -459,6 +474,14 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   const int nblk = norm_bwd_blocks(N);
   const bool ln = kind == GPT_NORM_LAYERNORM;
 
+  // bf16: the input gradients through W_fc, W_o and W_qkv read transposed
+  // copies (k contiguous on both sides of those GEMMs); W_proj's is read as
+  // it lies (its wide tiles run as fast either way)
+  const bool wt = ty == GPT_DTYPE_BF16;
+  if (wt) {
+    const TransposeDesc td[3] = {{w->w_fc, b.wt_fc, 4 * C, C}, {w->w_o, b.wt_o, C, C}, {w->w_qkv, b.wt_qkv, 3 * C, C}};
+    RUN("weight_transpose", launch_transpose(td, 3, s));
+  }
   // MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
   GemmDesc g = lin_dgrad(d, dy, C, w->w_proj, 4 * C, EPI_GELU_BWD);
   g.out = b.du; g.ldc = 4 * C; g.aux = sv.u; g.ldaux = 4 * C;
@@ -470,7 +493,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   int nwg = 0;
   wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
   if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
-  g = lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
+  g = wt ? lin_dgrad_t(d, b.du, 4 * C, b.wt_fc, C, EPI_STORE) : lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
   wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
@@ -482,7 +505,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     if (cfg->bias) RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln2_b, accumulate, s));
   }
   // attention output projection
-  g = lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
+  g = wt ? lin_dgrad_t(d, b.dx1, C, b.wt_o, C, EPI_STORE) : lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
   g.out = b.dO; g.ldc = C;
   RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
   wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
@@ -501,7 +524,8 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
       RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, sv.cs, sv.qkv, sv.qkr, b.dqkv, s));
   }
   // fused QKV projection
-  g = lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
+  g = wt ? lin_dgrad_t(d, b.dqkv, 3 * C, b.wt_qkv, C, EPI_STORE)
+         : lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
   wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);

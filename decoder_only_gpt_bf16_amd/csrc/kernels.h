@@ -88,6 +88,15 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s);
 // gemm_group_scratch_bytes() bytes.
 constexpr int GEMM_GROUP_MAX = 4;
 size_t gemm_group_scratch_bytes(const GemmDesc* d, int n, int dtype);
+// bf16 transposes dst[c][r] = src[r][c] ([rows][cols] row-major in, [cols][rows]
+// out), up to TRANSPOSE_MAX in one launch; rows and cols multiples of 8
+constexpr int TRANSPOSE_MAX = 4;
+struct TransposeDesc {
+  const void* src;
+  void* dst;
+  int rows, cols;
+};
+hipError_t launch_transpose(const TransposeDesc* d, int n, hipStream_t s);
 hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
