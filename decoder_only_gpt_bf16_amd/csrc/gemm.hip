@@ -197,12 +197,16 @@ __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt
 // logical unit (P % 8) ^ f(row).
 template <int R, int NT>
 struct StageKc {
-  static constexpr int NL = R * 8 / NT;
+  // copy instructions per thread; when R * 8 units are not a multiple of the
+  // thread count, the last one is issued by the first waves only
+  static constexpr int NL = (R * 8 + NT - 1) / NT;
   static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
                                                 int k0, int kend) {
+    static_assert(R % 8 == 0, "tile rows a multiple of 8");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
+      if ((R * 8) % NT != 0 && NT / 64 * i + w >= R * 8 / 64) break;
       const int P = (NT / 64 * i + w) * 64 + lane;
       const int row = P >> 3;
       const int u = (P & 7) ^ swz128(row);
@@ -225,12 +229,13 @@ struct StageKc {
 template <int R, int NT>
 struct StageKm {
   static constexpr int UPR = R / 8;
-  static constexpr int NL = 64 * UPR / NT;
+  static constexpr int NL = (64 * UPR + NT - 1) / NT;  // as in StageKc
   static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
                                                 int k0, int kend) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
+      if ((64 * UPR) % NT != 0 && NT / 64 * i + w >= UPR) break;
       const int P = (NT / 64 * i + w) * 64 + lane;
       const int kr = P / UPR;
       const int c = (P % UPR) ^ swz_km<UPR>(kr);
@@ -297,7 +302,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   // (32 rows, or 16 when 32 would not fit in the 160 KB of a CU)
   constexpr int SR = NW * 32 * (WN + 4) * 4 <= 160 * 1024 ? 32 : 16;
   constexpr int EPI_UNITS = NW * SR * (WN + 4) / 4;
-  __shared__ uint4 lds[2 * STAGE_UNITS > EPI_UNITS ? 2 * STAGE_UNITS : EPI_UNITS];
+  // the fused RoPE / QK-norm epilogue stages 64-row x 256-column strips of
+  // the whole tile, double-buffered, with rows padded to QKP floats
+  constexpr int QKP = 260;
+  constexpr int QK_UNITS = EPI == EPI_QKNORM ? 2 * 64 * QKP / 4 : 0;
+  constexpr int LDS_UNITS0 = 2 * STAGE_UNITS > EPI_UNITS ? 2 * STAGE_UNITS : EPI_UNITS;
+  __shared__ uint4 lds[LDS_UNITS0 > QK_UNITS ? LDS_UNITS0 : QK_UNITS];
   using SA = Stage<A_KMAJ, BM, NT>;
   using SB = Stage<B_KMAJ, BN, NT>;
 
@@ -419,6 +429,128 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   wait_lds();
   block_barrier();
 
+  if constexpr (EPI == EPI_QKNORM) {
+    // RoPE, then QK-norm, on the q and k heads of the tile (p.N = 3 C, head
+    // dim 128: the tile's 256 columns are two heads).  Strip i of every wave
+    // (rows 32 i.. of its 128) is staged into a 64 x 256 block of LDS; eight
+    // threads then share each row: thread q owns the RoPE pairs 8 q .. 8 q + 7
+    // of both heads (columns 8 q.. and 64 + 8 q.. of each), so the rotation is
+    // thread-local, one (cos, sin) fetch serves both heads, and a head's sum
+    // of squares takes three exchanges within the eight.
+    static_assert(NW == 8 && WGM == 2 && BM == 256 && BN == 256, "fused RoPE / QK-norm: 256 x 256 tiles, 8 waves");
+    float* eb = reinterpret_cast<float*>(lds);
+    const int C3 = p.N / 3;
+    const int H = C3 / 128;
+    const int rr = wave * 8 + (lane >> 3);  // staged row 0..63
+    const int q = lane & 7;
+    int which[2];                           // 0 q, 1 k, 2 v; 3: beyond N (a last, single-head tile)
+    which[0] = n0 / C3;
+    which[1] = (n0 + 128) / C3;
+    const bool rot = p.qk_rope && (which[0] < 2 || which[1] < 2);
+    float bias[2][2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bias[h][0][e] = bias[h][1][e] = 0.0f;
+    if (p.bias) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (n0 + 128 * h >= p.N) continue;
+        const bf16* b = reinterpret_cast<const bf16*>(p.bias) + n0 + 128 * h + 8 * q;
+        Vec8<bf16>::load(b, bias[h][0]);
+        Vec8<bf16>::load(b + 64, bias[h][1]);
+      }
+    }
+    // (cos, sin) of the thread's 8 pairs for its row of strip i
+    auto cs_row = [&](int i) -> const float4* {
+      const int m = m0 + (rr >> 5) * WM + 32 * i + (rr & 31);
+      const int t = (m < p.M ? m : 0) % p.qk_T;
+      return reinterpret_cast<const float4*>(p.qk_cs + (long)t * 64 + 8 * q);
+    };
+    float4 cn[4];
+    if (rot) {
+      const float4* c = cs_row(0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cn[k] = c[k];
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float* e = eb + (i & 1) * 64 * QKP;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(e + ((wave % WGM) * 32 + lrow) * QKP + wn + 32 * j + 8 * g + 4 * lhalf) =
+              make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+      wait_lds();
+      block_barrier();
+      const int m = m0 + (rr >> 5) * WM + 32 * i + (rr & 31);
+      float v[2][2][8];  // [head][lo, hi][pair]
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float* er = e + rr * QKP + 128 * h + 64 * u + 8 * q;
+          const float4 a = *reinterpret_cast<const float4*>(er);
+          const float4 b = *reinterpret_cast<const float4*>(er + 4);
+          v[h][u][0] = a.x + bias[h][u][0]; v[h][u][1] = a.y + bias[h][u][1];
+          v[h][u][2] = a.z + bias[h][u][2]; v[h][u][3] = a.w + bias[h][u][3];
+          v[h][u][4] = b.x + bias[h][u][4]; v[h][u][5] = b.y + bias[h][u][5];
+          v[h][u][6] = b.z + bias[h][u][6]; v[h][u][7] = b.w + bias[h][u][7];
+        }
+      if (rot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (which[h] < 2) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float4 c = cn[k];  // pairs 2 k and 2 k + 1: (cos, sin, cos, sin)
+              const float l0 = v[h][0][2 * k], h0 = v[h][1][2 * k];
+              const float l1 = v[h][0][2 * k + 1], h1 = v[h][1][2 * k + 1];
+              v[h][0][2 * k] = fmaf(l0, c.x, -h0 * c.y);
+              v[h][1][2 * k] = fmaf(h0, c.x, l0 * c.y);
+              v[h][0][2 * k + 1] = fmaf(l1, c.z, -h1 * c.w);
+              v[h][1][2 * k + 1] = fmaf(h1, c.z, l1 * c.w);
+            }
+          }
+        }
+        if (i + 1 < TM) {
+          const float4* c = cs_row(i + 1);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cn[k] = c[k];
+        }
+      }
+      if (p.qk_norm) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ss = fmaf(v[h][0][k], v[h][0][k], fmaf(v[h][1][k], v[h][1][k], ss));
+          ss += __shfl_xor(ss, 1, 64);
+          ss += __shfl_xor(ss, 2, 64);
+          ss += __shfl_xor(ss, 4, 64);
+          if (which[h] < 2) {
+            const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { v[h][0][k] *= r; v[h][1][k] *= r; }
+            if (q == 0 && m < p.M)
+              p.qk_rstd[(long)which[h] * p.M * H + (long)m * H + ((n0 + 128 * h) % C3) / 128] = r;
+          }
+        }
+      }
+      if (m < p.M) {
+        bf16* o = reinterpret_cast<bf16*>(p.out) + (long)m * p.ldc + n0 + 8 * q;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (n0 + 128 * h >= p.N) continue;
+          Vec8<bf16>::store(o + 128 * h, v[h][0]);
+          Vec8<bf16>::store(o + 128 * h + 64, v[h][1]);
+        }
+      }
+    }
+    return;
+  }
+
   // Epilogue through LDS (free after the barrier above): each wave writes
   // one 32-row strip of its accumulators (lane: row lrow, columns
   // 32 j + 8 g + 4 lhalf + e) and reads it back as 8-column row vectors, so
@@ -426,8 +558,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   constexpr int PITCH = WN + 4;           // floats per staged row
   constexpr int LPR = WN / 8;             // 8-column vectors (lanes) per row in the read-back
   static_assert((SR * LPR) % 64 == 0, "read-back passes must cover whole rows");
-  static_assert((EPI != EPI_XENT_STATS && EPI != EPI_QKNORM) || (64 % LPR == 0 && SR == 32),
-                "row reductions need a row's lanes in one pass");
+  static_assert(EPI != EPI_XENT_STATS || (64 % LPR == 0 && SR == 32), "row reductions need a row's lanes in one pass");
   float* ep = reinterpret_cast<float*>(lds) + wave * (SR * PITCH);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -475,45 +606,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
         for (int o = LPR / 2; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
         if (m < p.M && lane % LPR == 0)
           p.part[(long)m * p.part_ld + p.part_off + (n0 + wn) / WN] = make_float2(mx, sm);
-      } else if constexpr (EPI == EPI_QKNORM) {
-        // the wave's 128 columns are one head of q, k or v (p.N = 3 C); a
-        // row is spread over 16 lanes of 8 columns, RoPE partners
-        // (i, i + 64) sit 8 lanes apart
-        static_assert(WN == 128, "fused RoPE / QK-norm needs one 128-wide head per wave");
-        const int C3 = p.N / 3;
-        const int which = (n0 + wn) / C3;
-        if (p.bias && n < p.N) {
-          float t8[8];
-          Vec8<bf16>::load(reinterpret_cast<const bf16*>(p.bias) + n, t8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += t8[e];
-        }
-        if (which < 2) {
-          float ss = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
-          const float r = p.qk_norm ? 1.0f / sqrtf(ss * (1.0f / 128.0f) + p.qk_eps) : 1.0f;
-          if (p.qk_rope) {
-            const int t = (m < p.M ? m : 0) % p.qk_T;
-            const bool lo = col < 64;
-            const float2* cs = p.qk_cs + (long)t * 64 + (col & 63);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float w2 = __shfl_xor(v[e], 8, 64);
-              const float2 c = cs[e];
-              v[e] = lo ? fmaf(v[e], c.x, -w2 * c.y) : fmaf(w2, c.y, v[e] * c.x);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= r;
-          if (p.qk_norm && (lane & 15) == 0 && m < p.M && n < p.N) {
-            const int H = C3 / 128;
-            p.qk_rstd[(long)which * p.M * H + (long)m * H + ((n0 + wn) % C3) / 128] = r;
-          }
-        }
-        if (m < p.M && n < p.N) Vec8<bf16>::store(reinterpret_cast<bf16*>(p.out) + (long)m * p.ldc + n, v);
       } else {
         if (part) {
           float* d = part + (long)(m - m0) * BN + (n - n0);
@@ -738,9 +830,7 @@ Plan plan_mfma(const GemmDesc& d) {
 template <bool AK, bool BKm, int EPI, int BMv, int BNv>
 hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  if constexpr (BMv == 256 && EPI == EPI_QKNORM)
-    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 4>), grid, dim3(512), 0, s, p);
-  else if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
+  if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2>), grid, dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2>), grid, dim3(256), 0, s, p);
@@ -767,7 +857,7 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
       return hipErrorInvalidValue;
     } else {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
-      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 160, 4, 4>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 160, 8, 8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
     }
   }
