@@ -73,10 +73,22 @@ __device__ __forceinline__ void storeW(T* p, const float* f) {
 // Elementwise epilogue for W consecutive columns n..n+W-1 of row m.  Partial
 // vectors (n + W > N) take the same arithmetic with guarded element access.
 template <typename T, int EPI, int W>
-__device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v) {
+__device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v, bool use_pre = false,
+                                     uint4 pre = uint4{}) {
   if (m >= p.M || n >= p.N) return;
   const bool full = (n + W <= p.N);
   float t[W];
+  // use_pre: pre holds the row vector of resid (EPI_STORE) or aux
+  // (EPI_GELU_BWD) at (m, n), loaded ahead by the caller (bf16, W == 8, full
+  // vectors only)
+  auto take_pre = [&](float* f) {
+    const uint32_t w4[4] = {pre.x, pre.y, pre.z, pre.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w4[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+    }
+  };
   if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
     if (p.bias) {
       const T* b = reinterpret_cast<const T*>(p.bias) + n;
@@ -88,7 +100,8 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
   if constexpr (EPI == EPI_STORE) {
     if (p.resid) {
       const T* r = reinterpret_cast<const T*>(p.resid) + (long)m * p.ldr + n;
-      if (full) loadW<T, W>(r, t);
+      if (full && use_pre) take_pre(t);
+      else if (full) loadW<T, W>(r, t);
       else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(r[e]) : 0.0f;
       for (int e = 0; e < W; ++e) v[e] += t[e];
     }
@@ -102,7 +115,8 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
     else for (int e = 0; e < W; ++e) if (n + e < p.N) o2[e] = from_f32<T>(g[e]);
   } else if constexpr (EPI == EPI_GELU_BWD) {
     const T* dg = reinterpret_cast<const T*>(p.aux) + (long)m * p.ldaux + n;
-    if (full) loadW<T, W>(dg, t);
+    if (full && use_pre) take_pre(t);
+    else if (full) loadW<T, W>(dg, t);
     else for (int e = 0; e < W; ++e) t[e] = (n + e < p.N) ? to_f32(dg[e]) : 0.0f;
     for (int e = 0; e < W; ++e) v[e] *= t[e];
   } else if constexpr (EPI == EPI_XENT_GRAD) {
@@ -573,7 +587,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
               make_float4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
     }
     __builtin_amdgcn_wave_barrier();
-    for (int pass = 0; pass < SR * LPR / 64; ++pass) {
+    // resid / GELU'(u) row vectors of every pass are fetched before the first
+    // store, so their latencies overlap (the compiler may not move a load
+    // across a store to the output, which could alias it)
+    constexpr int NPASS = SR * LPR / 64;
+    constexpr bool PRE = EPI == EPI_STORE || EPI == EPI_GELU_BWD;
+    const bf16* pre_src = nullptr;
+    long pre_ld = 0;
+    if constexpr (EPI == EPI_STORE) { pre_src = reinterpret_cast<const bf16*>(p.resid); pre_ld = p.ldr; }
+    if constexpr (EPI == EPI_GELU_BWD) { pre_src = reinterpret_cast<const bf16*>(p.aux); pre_ld = p.ldaux; }
+    uint4 pre[PRE ? NPASS : 1];
+    if constexpr (PRE) {
+      if (pre_src && !part) {
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+          const int item = pass * 64 + lane;
+          const int m = m0 + wm + 32 * i + h * SR + item / LPR;
+          const int n = n0 + wn + (item % LPR) * 8;
+          pre[pass] = (m < p.M && n + 8 <= p.N) ? *reinterpret_cast<const uint4*>(pre_src + (long)m * pre_ld + n)
+                                                : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
       const int item = pass * 64 + lane;
       const int row = h * SR + item / LPR;  // row within the 32-row strip
       const int col = (item % LPR) * 8;
@@ -612,7 +649,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
           reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
           reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
         } else {
-          epiW<bf16, EPI, 8>(p, m, n, v);
+          epiW<bf16, EPI, 8>(p, m, n, v, PRE && pre_src, pre[PRE ? pass : 0]);
         }
       }
     }
