@@ -927,7 +927,9 @@ GemmParams make_params(const GemmDesc& d) {
 // (blocks [start[j], start[j + 1]) cover matrix j in 64-row x 256-column
 // tiles).  A thread moves one 8 x 8 block: 8 row vectors of 16 bytes in,
 // transposed in registers (halves of 32-bit words regrouped), 8 row vectors
-// of the transpose out.  Row and column counts are multiples of 8.
+// of the transpose out.  A wave covers 64 x 64 elements as 8 x 8 such
+// blocks, so that both its loads and its stores are whole 128-byte rows of
+// 8 lanes.  Row and column counts are multiples of 8.
 struct TransposeJobs {
   const bf16* src[TRANSPOSE_MAX];
   bf16* dst[TRANSPOSE_MAX];
@@ -941,8 +943,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_k(TransposeJobs J) {
   while (j + 1 < J.n && (int)blockIdx.x >= J.start[j + 1]) ++j;
   const int tid = blockIdx.x - J.start[j];
   const int R = J.rows[j], Cc = J.cols[j];
-  const int r = (tid / J.tiles_c[j]) * 64 + 8 * (threadIdx.x >> 5);
-  const int c = (tid % J.tiles_c[j]) * 256 + 8 * (threadIdx.x & 31);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = (tid / J.tiles_c[j]) * 64 + 8 * (lane >> 3);
+  const int c = (tid % J.tiles_c[j]) * 256 + 64 * wave + 8 * (lane & 7);
   if (r >= R || c >= Cc) return;
   const bf16* src = J.src[j] + (long)r * Cc + c;
   uint4 in[8];
