@@ -9,7 +9,10 @@ float64) and computes every step from its plain definition in NumPy float64.
 Sources (pages, by title):
   * "nanoGPT — Karpathy's minimal GPT pretraining repo": model.py section
     (GPTConfig, Block, CausalSelfAttention, MLP, LayerNorm, weight tying,
-    scaled residual init) and train.py section (shifted targets, mean loss).
+    scaled residual init, configure_optimizers: AdamW with decay on 2-D
+    tensors only) and train.py section (shifted targets, mean loss, gradient
+    clipping to a global norm of 1.0).  AdamW's own steps follow Loshchilov &
+    Hutter, "Decoupled Weight Decay Regularization", Algorithm 2.
   * "Train your own ChatGPT" (nanochat lab): 6.2, the loss_eval.py paragraph
     (bits per byte, zero-byte special tokens excluded); 6.3 (masked loss).
   * "nanochat-d20-chat — a chat model trained from scratch": Architecture row

@@ -29,7 +29,7 @@ __all__ = [
     "linear_fwd", "linear_bwd", "causal_attention_fwd", "causal_attention_bwd",
     "block_fwd", "block_bwd", "embed_fwd", "embed_bwd",
     "xent_fwd_bwd", "val_bpb", "model_fwd_bwd", "model_eval_nats",
-    "norm_fwd", "norm_bwd",
+    "norm_fwd", "norm_bwd", "clip_scale", "adamw_step",
 ]
 
 
@@ -446,3 +446,42 @@ def model_eval_nats(cfg, ids, targets, P):
     N = ids.size
     _, nats, _, _ = xent_fwd_bwd(hf.reshape(N, -1), W, targets.reshape(-1), 1.0, want_grad=False)
     return nats
+
+
+# ----------------------------------------------------------------------------
+# Optimizer step.
+# nanoGPT page, model.py section (configure_optimizers): AdamW with weight
+# decay on every 2-D tensor and none on 1-D tensors; train.py section:
+# gradients clipped to a global norm of 1.0 before the step.  The pages name
+# AdamW without restating it; the steps below are the decoupled-weight-decay
+# Adam of Loshchilov & Hutter ("Decoupled Weight Decay Regularization",
+# Algorithm 2, with the bias-corrected moments of Adam), in the order
+# PyTorch's AdamW applies them: decay of the old parameter, then the Adam
+# step.  Readings: clipping multiplies every gradient by max_norm / ||g||
+# when the global L2 norm ||g|| exceeds max_norm (no further epsilon);
+# beta1, beta2, eps, the decay rate and the learning rate are caller inputs
+# (the pages fix none of them).
+# ----------------------------------------------------------------------------
+
+def clip_scale(grads, max_norm):
+    """Global L2 norm over all gradient arrays and the factor that clips it."""
+    total = math.sqrt(sum(float(np.sum(np.asarray(g, dtype=np.float64) ** 2)) for g in grads))
+    if max_norm > 0 and total > max_norm:
+        return total, max_norm / total
+    return total, 1.0
+
+
+def adamw_step(p, g, m, v, step, lr, beta1, beta2, eps, weight_decay, decay, scale=1.0):
+    """One AdamW update of one tensor (float64).  step counts from 1.
+
+    Returns (p_new, m_new, v_new).  g is multiplied by the clip factor
+    `scale` first; `decay` selects weight decay for this tensor.
+    """
+    g = np.asarray(g, dtype=np.float64) * scale
+    m_new = beta1 * m + (1.0 - beta1) * g
+    v_new = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m_new / (1.0 - beta1 ** step)
+    v_hat = v_new / (1.0 - beta2 ** step)
+    p_new = p * (1.0 - lr * weight_decay) if decay else np.array(p, dtype=np.float64, copy=True)
+    p_new = p_new - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return p_new, m_new, v_new
