@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the GPT-2 block, GPT-2 step and d20 eval")
+    ap.add_argument("--adamw", action="store_true",
+                    help="also time the AdamW step over the d20 model's parameter set (HBM-bound)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
@@ -228,11 +230,49 @@ def main():
         "roofline": roof,
         "kernels": sites,
     }
-    if args.extra:
-        out["extra"] = extra_workloads(args)
+    if args.extra or args.adamw:
+        out["extra"] = extra_workloads(args) if args.extra else {}
+        out["extra"]["adamw_d20_model"] = adamw_workload(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def adamw_workload(args):
+    """AdamW + global-norm clip over the d20 model's parameters: 20 blocks of
+    (w_qkv, w_o, w_fc, w_proj), token embedding and untied head [32768, 1280],
+    fp32 state with a bf16 copy of every parameter.  Per element the step moves
+    34 bytes (gradient read twice, for the norm and the update; param, m, v
+    read and written; bf16 copy written)."""
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    from decoder_only_gpt_bf16_amd import synth
+    cfg = synth.D20_BLOCK.cfg
+    shapes = [s for _ in range(20) for _, s in synth.block_param_shapes(cfg)] + [(32768, cfg.n_embd)] * 2
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    ts = []
+    for shp in shapes:
+        ts.append({"param": 0.02 * torch.randn(shp, generator=gen, device="cuda"),
+                   "grad": 1e-4 * torch.randn(shp, generator=gen, device="cuda"),
+                   "m": torch.zeros(shp, device="cuda"), "v": torch.zeros(shp, device="cuda"),
+                   "param_bf16": torch.empty(shp, dtype=torch.bfloat16, device="cuda"), "decay": True})
+    n = sum(t["param"].numel() for t in ts)
+    ws = torch.empty(B.gpt_adamw_workspace_bytes(ts), dtype=torch.uint8, device="cuda")
+    norm = torch.zeros(4, device="cuda")
+    it = [0]
+
+    def step():
+        it[0] += 1
+        B.gpt_adamw_step(ts, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=it[0],
+                         max_norm=1.0, grad_norm=norm, ws=ws)
+
+    ms = time_steps(step, max(3, args.steps // 2), 2)
+    byts = 34.0 * n
+    res = {"params": n, "tensors": len(ts), "ms": ms, "bytes_per_step": byts,
+           "achieved_GBps": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / PEAK_HBM}
+    del ts, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def extra_workloads(args):

@@ -42,9 +42,22 @@ class BlockGradsC(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in BLOCK_FIELDS]
 
 
+class AdamwTensorC(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("param_bf16", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("decay", ctypes.c_int32)]
+
+
+class AdamwConfigC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("max_norm", ctypes.c_float)]
+
+
 _lib = None
 _VP, _I, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
 _CFG = ctypes.POINTER(GptConfigC)
+_ATP = ctypes.POINTER(AdamwTensorC)
 
 _SIGS = {
     "gpt_block_saved_bytes": (_SZ, [_CFG, _I, _I]),
@@ -58,6 +71,8 @@ _SIGS = {
     "gpt_embed_bwd": (_I, [_CFG, _I, _I, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
     "gpt_norm_fwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
     "gpt_norm_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "gpt_adamw_step": (_I, [ctypes.POINTER(AdamwConfigC), _ATP, _I, _VP, _VP, _SZ, _VP]),
+    "gpt_adamw_workspace_bytes": (_SZ, [_ATP, _I]),
     "gpt_trace_begin": (_I, [_I]),
     "gpt_trace_end": (_I, [ctypes.c_char_p, _SZ]),
     "gpt_status_string": (ctypes.c_char_p, [_I]),
@@ -213,3 +228,35 @@ def gpt_norm_bwd(cfg, N, x, w, dy, resid, dx, dw, db, accumulate, ws, stream=Non
     _check(lib().gpt_norm_bwd(ctypes.byref(cfg), N, _p(x, cfg), _p(w, cfg), _p(dy, cfg), _p(resid, cfg), _p(dx, cfg),
                               _p(dw, "f32"), _p(db, "f32"),
                               int(accumulate), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def _adamw_table(tensors):
+    """tensors: iterable of dicts with param, grad, m, v (fp32), optional
+    param_bf16 (bf16) and decay (bool)."""
+    tensors = list(tensors)
+    arr = (AdamwTensorC * len(tensors))()
+    for i, t in enumerate(tensors):
+        n = t["param"].numel()
+        for k in ("grad", "m", "v"):
+            if t[k].numel() != n:
+                raise ValueError(f"tensor {i}: {k} has {t[k].numel()} elements, param has {n}")
+        p16 = t.get("param_bf16")
+        if p16 is not None:
+            import torch
+            if p16.dtype != torch.bfloat16 or p16.numel() != n:
+                raise TypeError(f"tensor {i}: param_bf16 must be a bf16 tensor of {n} elements")
+        arr[i] = AdamwTensorC(_p(t["param"], "f32"), _p(t["grad"], "f32"), _p(t["m"], "f32"), _p(t["v"], "f32"),
+                              _p(p16), n, int(bool(t.get("decay", True))))
+    return arr
+
+
+def gpt_adamw_workspace_bytes(tensors) -> int:
+    arr = _adamw_table(tensors)
+    return lib().gpt_adamw_workspace_bytes(arr, len(arr))
+
+
+def gpt_adamw_step(tensors, lr, beta1, beta2, eps, weight_decay, step, max_norm, grad_norm, ws, stream=None):
+    arr = _adamw_table(tensors)
+    cfg = AdamwConfigC(lr, beta1, beta2, eps, weight_decay, int(step), max_norm)
+    _check(lib().gpt_adamw_step(ctypes.byref(cfg), arr, len(arr), _p(grad_norm, "f32"), _p(ws), _nbytes(ws),
+                                _stream(stream)))

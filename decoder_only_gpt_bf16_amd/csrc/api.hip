@@ -1,6 +1,7 @@
 // C ABI of the library (declared in include/gptmi.h): argument validation,
 // saved-activation and workspace planning, and the launch sequence of each
 // entry point on the caller's stream.  No allocation, no synchronisation.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -625,6 +626,53 @@ int val_bpb_reduce(int N, const float* nats, const int32_t* targets, const int32
     return fail(GPT_ERR_INVALID, "a pointer argument is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   RUN("bpb", launch_bpb(N, V, nats, targets, token_bytes, sum_nats, sum_bytes, s));
+  return GPT_OK;
+}
+
+// ------------------------------------------------------------ optimizer
+static int adamw_tensors(const gpt_adamw_tensor* tensors, int count, std::vector<OptTensor>& out) {
+  if (!tensors || count <= 0) return fail(GPT_ERR_INVALID, "no tensors");
+  out.resize(count);
+  for (int i = 0; i < count; ++i) {
+    const gpt_adamw_tensor& t = tensors[i];
+    if (!t.param || !t.grad || !t.m || !t.v) return fail(GPT_ERR_INVALID, "tensor %d: a pointer is NULL", i);
+    if (t.n <= 0) return fail(GPT_ERR_INVALID, "tensor %d: n must be positive", i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.m) || !aligned16(t.v) ||
+        !aligned16(t.param_bf16))
+      return fail(GPT_ERR_INVALID, "tensor %d: pointer not 16-byte aligned", i);
+    out[i] = OptTensor{t.param, t.grad, t.m, t.v, t.param_bf16, (long)t.n, t.decay ? 1 : 0};
+  }
+  return GPT_OK;
+}
+
+size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count) {
+  std::vector<OptTensor> t;
+  if (adamw_tensors(tensors, count, t)) return 0;
+  return adamw_ws_bytes(t.data(), count);
+}
+
+int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors, int count, float* grad_norm,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (!cfg) return fail(GPT_ERR_INVALID, "cfg is NULL");
+  const float hp[] = {cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, cfg->max_norm};
+  for (float x : hp)
+    if (!std::isfinite(x)) return fail(GPT_ERR_INVALID, "non-finite hyperparameter");
+  if (cfg->step < 1) return fail(GPT_ERR_INVALID, "step must be >= 1");
+  if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f))
+    return fail(GPT_ERR_INVALID, "betas must lie in [0, 1)");
+  if (cfg->eps < 0.0f || cfg->lr < 0.0f || cfg->weight_decay < 0.0f)
+    return fail(GPT_ERR_INVALID, "lr, eps and weight_decay must be non-negative");
+  if (cfg->eps == 0.0f && cfg->beta2 == 0.0f) return fail(GPT_ERR_INVALID, "eps = 0 needs beta2 > 0");
+  std::vector<OptTensor> t;
+  int st = adamw_tensors(tensors, count, t);
+  if (st) return st;
+  if (adamw_chunks(t.data(), count) > (1L << 30)) return fail(GPT_ERR_UNSUPPORTED, "parameter set too large");
+  const size_t need = adamw_ws_bytes(t.data(), count);
+  if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+  if (!aligned16(ws) || !aligned16(grad_norm)) return fail(GPT_ERR_INVALID, "ws or grad_norm not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("adamw", launch_adamw(t.data(), count, cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
+                            cfg->step, cfg->max_norm, grad_norm, ws, s));
   return GPT_OK;
 }
 

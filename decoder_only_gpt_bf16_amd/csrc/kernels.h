@@ -184,3 +184,22 @@ hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t s);
 // targets outside [0, V) count as zero-byte tokens.
 hipError_t launch_bpb(int N, int V, const float* nats, const int32_t* targets, const int32_t* token_bytes,
                       double* sum_nats, int64_t* sum_bytes, hipStream_t s);
+
+// AdamW with global-norm clipping over a set of fp32 tensors (optim.hip).
+constexpr int OPT_TABLE = 32;  // tensors per launch
+struct OptTensor {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  void* p16;  // bf16 copy of the updated parameter, or nullptr
+  long n;
+  int decay;
+};
+long adamw_chunks(const OptTensor* t, int count);
+size_t adamw_ws_bytes(const OptTensor* t, int count);
+// max_norm <= 0: no clipping.  norm_out (device, optional) receives the global
+// gradient norm before clipping.  ws: adamw_ws_bytes bytes.
+hipError_t launch_adamw(const OptTensor* t, int count, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, int step, float max_norm, float* norm_out, void* ws,
+                        hipStream_t s);

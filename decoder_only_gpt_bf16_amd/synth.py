@@ -19,7 +19,11 @@ Recipe (all draws float64 from numpy's PCG64):
     p(k) proportional to k^-s, id = k-1, by inverse-CDF sampling;
     targets are the ids shifted by one (draw [B, T+1], x = [:, :T],
     y = [:, 1:]; nanoGPT page, train.py section);
-  * token byte lengths: one value per vocabulary entry, uniform in 1..12.
+  * token byte lengths: one value per vocabulary entry, uniform in 1..12;
+  * optimizer state (make_adamw_inputs): per tensor, param ~ N(0, 0.02^2),
+    grad ~ N(0, g_std^2), first moment ~ N(0, (0.1 g_std)^2), second moment
+    = (N(0, g_std^2))^2, all fp32; tensor j drawn from
+    default_rng([100, seed, j]).
 Rounding: float64 -> float32 (round to nearest even) -> bf16 (round to
 nearest even on the float32 bits).
 """
@@ -260,3 +264,35 @@ def oracle_cfg(cfg: GPTConfig) -> dict:
                 vocab_size=cfg.vocab_size, norm=cfg.norm, bias=cfg.bias,
                 rope=cfg.rope, qk_norm=cfg.qk_norm, rope_base=cfg.rope_base,
                 eps=cfg.eps)
+
+
+def make_adamw_inputs(shapes, seed: int = 0, g_std: float = 1e-2):
+    """fp32-representable float64 arrays (param, grad, m, v) per shape."""
+    out = []
+    for j, shp in enumerate(shapes):
+        rng = np.random.default_rng([100, seed, j])
+        p = round_to(rng.normal(0.0, 0.02, shp), "fp32")
+        g = round_to(rng.normal(0.0, g_std, shp), "fp32")
+        m = round_to(rng.normal(0.0, 0.1 * g_std, shp), "fp32")
+        v = round_to(rng.normal(0.0, g_std, shp) ** 2, "fp32")
+        out.append((p, g, m, v))
+    return out
+
+
+def block_param_shapes(cfg: "GPTConfig"):
+    """(shape, is 2-D) of one block's parameters in BLOCK_FIELDS order, biases
+    and norm gains included only where the configuration has them."""
+    C = cfg.n_embd
+    ln = cfg.norm == "layernorm"
+    out = []
+    for name, shp in (("ln1_w", (C,)), ("ln1_b", (C,)), ("w_qkv", (3 * C, C)), ("b_qkv", (3 * C,)),
+                      ("w_o", (C, C)), ("b_o", (C,)), ("ln2_w", (C,)), ("ln2_b", (C,)),
+                      ("w_fc", (4 * C, C)), ("b_fc", (4 * C,)), ("w_proj", (C, 4 * C)), ("b_proj", (C,))):
+        if name.startswith("ln") and not ln:
+            continue
+        if name.endswith("_b") and not (ln and cfg.bias):
+            continue
+        if name.startswith("b_") and not cfg.bias:
+            continue
+        out.append((name, shp))
+    return out

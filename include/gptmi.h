@@ -162,6 +162,48 @@ int val_bpb_reduce(int N, const float* nats, const int32_t* targets,
                    const int32_t* token_bytes, int V, double* sum_nats,
                    int64_t* sum_bytes, void* stream);
 
+/* ---- optimizer step ---- */
+
+/* One tensor of a parameter set.  All device pointers, 16-byte aligned; the
+ * tensors of one call must not overlap. */
+typedef struct {
+  float* param;        /* fp32 [n], updated in place                          */
+  const float* grad;   /* fp32 [n], as the backward entry points write them  */
+  float* m;            /* fp32 [n] first moment, in place (zeros at step 1)   */
+  float* v;            /* fp32 [n] second moment, in place (zeros at step 1)  */
+  void* param_bf16;    /* bf16 [n] copy of the updated param, or NULL         */
+  int64_t n;           /* elements, > 0                                        */
+  int32_t decay;       /* 1: weight decay applies (2-D tensors), 0: none      */
+} gpt_adamw_tensor;
+
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t step;        /* 1 for the first update                              */
+  float max_norm;      /* clip of the global gradient norm; <= 0: no clip     */
+} gpt_adamw_config;
+
+/* AdamW step over `count` tensors ([nanoGPT] model.py section,
+ * configure_optimizers: weight decay on every 2-D tensor, none on 1-D ones;
+ * train.py section: the gradients are clipped to a global norm, 1.0 there,
+ * before the step).  With ||g|| the L2 norm over all `grad` arrays and
+ * s = max_norm / ||g|| when max_norm > 0 and ||g|| > max_norm (else 1), each
+ * element takes, in fp32 (t = step; Loshchilov & Hutter, "Decoupled Weight
+ * Decay Regularization", Algorithm 2, in PyTorch's AdamW order):
+ *   g' = s g;  m = b1 m + (1 - b1) g';  v = b2 v + (1 - b2) g'^2;
+ *   p = p (1 - lr wd)   [decay tensors only];
+ *   p = p - lr / (1 - b1^t) * m / (sqrt(v) / sqrt(1 - b2^t) + eps);
+ * and param_bf16 (when given) receives p rounded to bf16.  `tensors` is a
+ * HOST array read during the call.  grad_norm: optional device fp32 scalar
+ * that receives ||g|| (before clipping).  The norm is summed in fp64 in a
+ * fixed order, so results are bitwise reproducible.  ws: device workspace of
+ * gpt_adamw_workspace_bytes(tensors, count) bytes.  The hyperparameters are
+ * inputs; the pages fix only the decay grouping and the clip.
+ * Errors: INVALID, WORKSPACE, HIP. */
+int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors,
+                   int count, float* grad_norm, void* ws, size_t ws_bytes,
+                   void* stream);
+size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count);
+
 /* ---- helpers used to assemble a full model step (same conventions) ---- */
 
 /* x0[n] = wte[ids[n]] (+ wpe[t] with learned positions, cfg->rope == 0).

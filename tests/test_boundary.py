@@ -161,3 +161,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_adamw_validation_without_gpu():
+    """Argument checks run before any launch, so fake aligned addresses do."""
+    import ctypes
+    L = B.lib()
+    t = (B.AdamwTensorC * 2)()
+    t[0] = B.AdamwTensorC(16, 32, 48, 64, None, 100, 1)
+    t[1] = B.AdamwTensorC(80, 96, 112, 128, 144, 5, 0)
+    need = L.gpt_adamw_workspace_bytes(t, 2)
+    assert need >= 2 * 8
+    ok = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1, max_norm=1.0)
+
+    def call(cfg=None, count=2, ws=256, nbytes=None, tensors=t):
+        c = B.AdamwConfigC(**{**ok, **(cfg or {})})
+        return L.gpt_adamw_step(ctypes.byref(c), tensors, count, None, ws, need if nbytes is None else nbytes, None)
+
+    assert call({"step": 0}) == B.GPT_ERR_INVALID
+    assert call({"beta1": 1.0}) == B.GPT_ERR_INVALID
+    assert call({"lr": float("nan")}) == B.GPT_ERR_INVALID
+    assert call({"eps": -1.0}) == B.GPT_ERR_INVALID
+    assert call(count=0) == B.GPT_ERR_INVALID
+    assert call(nbytes=need - 1) == B.GPT_ERR_WORKSPACE
+    assert call(ws=0) == B.GPT_ERR_WORKSPACE
+    bad = (B.AdamwTensorC * 1)()
+    bad[0] = B.AdamwTensorC(17, 32, 48, 64, None, 100, 1)
+    assert call(count=1, tensors=bad) == B.GPT_ERR_INVALID
+    bad[0] = B.AdamwTensorC(16, 32, 48, 64, None, 0, 1)
+    assert call(count=1, tensors=bad) == B.GPT_ERR_INVALID
+    bad[0] = B.AdamwTensorC(16, None, 48, 64, None, 4, 1)
+    assert call(count=1, tensors=bad) == B.GPT_ERR_INVALID
