@@ -344,13 +344,19 @@ def embed_bwd(dx0, ids, V, wpe_rows):
 # makes the head weight the token embedding).
 # ----------------------------------------------------------------------------
 
-def xent_fwd_bwd(h, W, targets, scale, want_grad=True, row_chunk=2048):
+def xent_fwd_bwd(h, W, targets, scale, want_grad=True, row_chunk=2048, weights=None):
     """h: [N, C]; W: [V, C]; targets: int [N].
 
     nats_n = logsumexp(z_n) - z_n[y_n] with z = h W^T; loss = scale * sum nats.
     With want_grad: dz = (softmax(z) - onehot(y)) * scale, dh = dz W,
     dW = dz^T h.  Rows are processed in chunks only to bound memory; each row
     is complete (all V logits) inside its chunk.
+
+    weights (float [N], optional) weight each token: loss = scale * sum
+    w_n nats_n and row n of dz carries scale * w_n.  With w the 0/1 mask of
+    the tokens to learn and scale = 1 / sum(mask) this is the masked mean of
+    the chat fine-tuning stage ("Train your own ChatGPT", section 6.3: the
+    per-token losses times the mask, summed, over the mask's sum).
     """
     N, C = h.shape
     nats = np.empty(N)
@@ -369,9 +375,14 @@ def xent_fwd_bwd(h, W, targets, scale, want_grad=True, row_chunk=2048):
             dz = e / s
             dz[rows, targets[r0:r1]] -= 1.0
             dz *= scale
+            if weights is not None:
+                dz *= np.asarray(weights[r0:r1], dtype=np.float64)[:, None]
             dh[r0:r1] = dz @ W
             dW += dz.T @ h[r0:r1]
-    loss = scale * nats.sum()
+    if weights is None:
+        loss = scale * nats.sum()
+    else:
+        loss = scale * float(np.dot(np.asarray(weights, dtype=np.float64), nats))
     return loss, nats, dh, dW
 
 

@@ -176,3 +176,17 @@ def test_model_fwd_bwd_fd(form):
             if val is None:
                 continue
             _check(lambda t, li=li, name=name: L_of(None, t, li, name), val, G["blocks"][li][name], rng, n_dirs=1)
+
+
+def test_xent_weighted_fd():
+    rng = np.random.default_rng(16)
+    N, C, V = 9, 6, 11
+    h = rng.standard_normal((N, C))
+    W = rng.standard_normal((V, C))
+    y = rng.integers(0, V, N)
+    w = rng.uniform(0.0, 2.0, N)
+    w[3] = 0.0
+    _, _, dh, dW = O.xent_fwd_bwd(h, W, y, 0.37, row_chunk=4, weights=w)
+    _check(lambda t: O.xent_fwd_bwd(t, W, y, 0.37, want_grad=False, weights=w)[0], h, dh, rng)
+    _check(lambda t: O.xent_fwd_bwd(h, t, y, 0.37, want_grad=False, weights=w)[0], W, dW, rng)
+    assert not dh[3].any()

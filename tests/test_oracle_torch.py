@@ -157,3 +157,30 @@ def test_model_step_matches_torch_autograd(form):
         for k, v in blocks[li].items():
             if v is not None:
                 assert _rel(G["blocks"][li][k], v.grad.numpy()) < 1e-10, (li, k)
+
+
+def test_masked_xent_matches_torch():
+    """The masked mean of the chat fine-tuning stage: per-token losses times
+    the mask, summed, divided by the mask's sum (float64 autograd)."""
+    rng = np.random.default_rng(21)
+    N, C, V = 40, 16, 37
+    h = rng.standard_normal((N, C))
+    W = 0.3 * rng.standard_normal((V, C))
+    y = rng.integers(0, V, N)
+    mask = (rng.uniform(size=N) < 0.6).astype(np.float64)
+    th = torch.tensor(h, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    losses = F.cross_entropy(th @ tW.T, torch.tensor(y), reduction="none")
+    tm = torch.tensor(mask)
+    loss_t = (losses * tm).sum() / tm.sum()
+    loss_t.backward()
+    loss, nats, dh, dW = O.xent_fwd_bwd(h, W, y, 1.0 / mask.sum(), weights=mask)
+    assert loss == pytest.approx(loss_t.item(), rel=1e-12)
+    np.testing.assert_allclose(nats, losses.detach().numpy(), rtol=1e-12)
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=1e-10, atol=1e-14)
+    # all-ones weights give the unweighted loss exactly
+    l1, _, dh1, _ = O.xent_fwd_bwd(h, W, y, 1.0 / N, weights=np.ones(N))
+    l0, _, dh0, _ = O.xent_fwd_bwd(h, W, y, 1.0 / N)
+    assert l1 == pytest.approx(l0, rel=1e-15)
+    np.testing.assert_array_equal(dh1, dh0)
