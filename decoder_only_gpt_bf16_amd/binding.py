@@ -66,6 +66,8 @@ _SIGS = {
     "gpt_block_bwd": (_I, [_CFG, _I, _I, _VP, _VP, ctypes.POINTER(BlockWeightsC), _VP, _VP,
                            ctypes.POINTER(BlockGradsC), _I, _VP, _SZ, _VP]),
     "lm_head_xent_fwd_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
+    "lm_head_xent_weighted_fwd_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP, _I, _VP, _SZ,
+                                           _VP]),
     "val_bpb_reduce": (_I, [_I, _VP, _VP, _VP, _I, _VP, _VP, _VP]),
     "gpt_embed_fwd": (_I, [_CFG, _I, _I, _VP, _VP, _VP, _VP, _VP]),
     "gpt_embed_bwd": (_I, [_CFG, _I, _I, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
@@ -185,6 +187,14 @@ def lm_head_xent_fwd_bwd(cfg, N, h, W, targets, loss_scale, loss, nats, dh, dW, 
                                       float(loss_scale), _p(loss, "f32"), _p(nats, "f32"), _p(dh, cfg),
                                       _p(dW, "f32"), int(accumulate), _p(ws), _nbytes(ws),
                                       _stream(stream)))
+
+
+def lm_head_xent_weighted_fwd_bwd(cfg, N, h, W, targets, token_weight, loss_scale, loss, nats, dh, dW, accumulate,
+                                  ws, stream=None):
+    _check(lib().lm_head_xent_weighted_fwd_bwd(ctypes.byref(cfg), N, _p(h, cfg), _p(W, cfg), _p(targets, "i32"),
+                                               _p(token_weight, "f32"), float(loss_scale), _p(loss, "f32"),
+                                               _p(nats, "f32"), _p(dh, cfg), _p(dW, "f32"), int(accumulate),
+                                               _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def val_bpb_reduce(N, nats, targets, token_bytes, V, sum_nats, sum_bytes, stream=None):

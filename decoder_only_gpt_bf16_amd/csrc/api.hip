@@ -541,9 +541,9 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   return GPT_OK;
 }
 
-int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void* W, const int32_t* targets,
-                         float loss_scale, float* loss, float* nats, void* dh, float* dW, int accumulate, void* ws,
-                         size_t ws_bytes, void* stream) {
+static int xent_impl(const gpt_config* cfg, int N, const void* h, const void* W, const int32_t* targets,
+                     const float* weight, float loss_scale, float* loss, float* nats, void* dh, float* dW,
+                     int accumulate, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   int st = check_cfg(cfg, d);
   if (st) return st;
@@ -581,7 +581,8 @@ int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void
       RUN("xent_rows_stats", launch_xent_rows_stats(N, Vw, v0, x.zbuf, x.ldz, targets, x.run, x.ztgt, c == 0, s));
     }
   }
-  RUN("xent_finish", launch_xent_finish(N, mfma ? x.P : 1, mfma ? x.part : x.run, x.ztgt, x.lse, nt, x.loss_part, s));
+  RUN("xent_finish",
+      launch_xent_finish(N, mfma ? x.P : 1, mfma ? x.part : x.run, x.ztgt, weight, x.lse, nt, x.loss_part, s));
   RUN("loss_sum", launch_loss_sum(xent_finish_blocks(N), x.loss_part, loss_scale, loss, s));
   if (!dh && !dW) return GPT_OK;
   for (int c = 0; c < x.nchunk; ++c) {
@@ -592,12 +593,13 @@ int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void
     g.A = h; g.lda = C; g.B = Wc; g.ldb = C; g.M = N; g.N = Vw; g.K = C;
     if (mfma) {
       g.epi = EPI_XENT_GRAD; g.out = x.dz; g.ldc = x.ldz;
-      g.tgt = targets; g.col_offset = v0; g.lse = x.lse; g.scale = loss_scale;
+      g.tgt = targets; g.col_offset = v0; g.lse = x.lse; g.scale = loss_scale; g.roww = weight;
       RUN("xent_grad_gemm", launch_gemm(g, ty, nullptr, s));
     } else {
       g.epi = EPI_F32; g.out = x.zbuf; g.ldc = x.ldz;
       RUN("xent_logits_gemm", launch_gemm(g, ty, nullptr, s));
-      RUN("xent_rows_grad", launch_xent_rows_grad(ty, N, Vw, v0, x.zbuf, x.ldz, targets, x.lse, loss_scale, x.dz, x.ldz, s));
+      RUN("xent_rows_grad",
+          launch_xent_rows_grad(ty, N, Vw, v0, x.zbuf, x.ldz, targets, x.lse, loss_scale, weight, x.dz, x.ldz, s));
     }
     if (dh) {
       GemmDesc q = gemm0();
@@ -617,6 +619,20 @@ int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void
   }
   if (dh) RUN("xent_dh_convert", launch_f32_to(ty, (long)N * C, x.dh_acc, dh, s));
   return GPT_OK;
+}
+
+int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void* W, const int32_t* targets,
+                         float loss_scale, float* loss, float* nats, void* dh, float* dW, int accumulate, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return xent_impl(cfg, N, h, W, targets, nullptr, loss_scale, loss, nats, dh, dW, accumulate, ws, ws_bytes, stream);
+}
+
+int lm_head_xent_weighted_fwd_bwd(const gpt_config* cfg, int N, const void* h, const void* W, const int32_t* targets,
+                                  const float* token_weight, float loss_scale, float* loss, float* nats, void* dh,
+                                  float* dW, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  if (!token_weight) return fail(GPT_ERR_INVALID, "token_weight is NULL");
+  return xent_impl(cfg, N, h, W, targets, token_weight, loss_scale, loss, nats, dh, dW, accumulate, ws, ws_bytes,
+                   stream);
 }
 
 int val_bpb_reduce(int N, const float* nats, const int32_t* targets, const int32_t* token_bytes, int V,

@@ -122,9 +122,10 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
   } else if constexpr (EPI == EPI_XENT_GRAD) {
     const float l = p.lse[m];
     const int tg = p.tgt[m] - p.col_offset;
+    const float sc = p.roww ? p.scale * p.roww[m] : p.scale;
     for (int e = 0; e < W; ++e) {
       const float pr = exp2f((v[e] - l) * LOG2E);
-      v[e] = (pr - (n + e == tg ? 1.0f : 0.0f)) * p.scale;
+      v[e] = (pr - (n + e == tg ? 1.0f : 0.0f)) * sc;
     }
   }
   if constexpr (EPI == EPI_F32) {
@@ -916,7 +917,7 @@ GemmParams make_params(const GemmDesc& d) {
   p.bias = d.bias; p.resid = d.resid; p.ldr = d.ldr; p.out2 = d.out2;
   p.aux = d.aux; p.ldaux = d.ldaux; p.accumulate = d.accumulate;
   p.tgt = d.tgt; p.col_offset = d.col_offset; p.part = d.part; p.part_ld = d.part_ld;
-  p.part_off = d.part_off; p.ztgt = d.ztgt; p.lse = d.lse; p.scale = d.scale;
+  p.part_off = d.part_off; p.ztgt = d.ztgt; p.lse = d.lse; p.scale = d.scale; p.roww = d.roww;
   p.qk_cs = d.qk_cs; p.qk_rstd = d.qk_rstd; p.qk_T = d.qk_T; p.qk_rope = d.qk_rope; p.qk_norm = d.qk_norm;
   p.qk_eps = d.qk_eps;
   return p;

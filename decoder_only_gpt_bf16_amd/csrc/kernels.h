@@ -19,7 +19,7 @@ enum EpiKind {
   EPI_GELU_BWD = 2,   // out(T) = acc * aux[m, n] (aux = the stored gelu'(u))
   EPI_F32 = 3,        // out(f32) = acc (+ out if accumulate)
   EPI_XENT_STATS = 4, // per (row, 128-col block): max and sum exp; target logit
-  EPI_XENT_GRAD = 5,  // out(T) = (exp(acc - lse[m]) - [n + col_offset == tgt[m]]) * scale
+  EPI_XENT_GRAD = 5,  // out(T) = (exp(acc - lse[m]) - [n + col_offset == tgt[m]]) * scale (* roww[m])
   EPI_QKNORM = 6,     // fused QKV (N = 3C, head_dim 128): out(T) = acc (+ bias), then RoPE and
                       // QK-norm on the q and k heads; 1 / rms of each into qk_rstd [2][M][H]
 };
@@ -52,6 +52,7 @@ struct GemmParams {
   float* ztgt;            // [M] target logits
   const float* lse;       // [M]
   float scale;
+  const float* roww;      // [M] per-row weight of EPI_XENT_GRAD, or nullptr
   // fused RoPE / QK-norm epilogue
   const float2* qk_cs;    // [T][64] (cos, sin)
   float* qk_rstd;
@@ -71,7 +72,7 @@ struct GemmDesc {
   const void* aux; long ldaux;
   int accumulate;
   const int32_t* tgt; int col_offset; float2* part; int part_ld; int part_off;
-  float* ztgt; const float* lse; float scale;
+  float* ztgt; const float* lse; float scale; const float* roww;
   const float2* qk_cs; float* qk_rstd; int qk_T, qk_rope, qk_norm; float qk_eps;
 };
 
@@ -166,7 +167,9 @@ bool attn_mfma_supported(int dtype, int D);
 
 // Cross-entropy reductions.
 // Combine per-row partials into lse, nats = lse - ztgt, block loss partials.
-hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, float* lse,
+// w (optional): per-token weights of the loss sum; a token of weight 0
+// contributes nothing (also when its target is out of range).
+hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, const float* w, float* lse,
                               float* nats, float* loss_part, hipStream_t s);
 hipError_t launch_loss_sum(int nblk, const float* loss_part, float scale, float* loss,
                            hipStream_t s);
@@ -176,7 +179,7 @@ hipError_t launch_xent_rows_stats(int N, int Vc, int v0, const float* z, long ld
                                   const int32_t* tgt, float2* run, float* ztgt, int first,
                                   hipStream_t s);
 hipError_t launch_xent_rows_grad(int dtype, int N, int Vc, int v0, const float* z, long ldz,
-                                 const int32_t* tgt, const float* lse, float scale, void* dz,
+                                 const int32_t* tgt, const float* lse, float scale, const float* w, void* dz,
                                  long lddz, hipStream_t s);
 hipError_t launch_f32_to(int dtype, long n, const float* src, void* dst, hipStream_t s);
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t s);

@@ -27,8 +27,9 @@ __device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
 // One wave per row: merge P partials -> lse; nats = lse - ztgt.  Per-block
 // sum of nats into loss_part[block] (waves in fixed order).
 __global__ __launch_bounds__(256) void xent_finish_k(int N, int P, const float2* __restrict__ part,
-                                                     const float* __restrict__ ztgt, float* __restrict__ lse,
-                                                     float* __restrict__ nats, float* __restrict__ loss_part) {
+                                                     const float* __restrict__ ztgt, const float* __restrict__ w,
+                                                     float* __restrict__ lse, float* __restrict__ nats,
+                                                     float* __restrict__ loss_part) {
   __shared__ float red[FINISH_ROWS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * FINISH_ROWS + wave;
@@ -51,7 +52,9 @@ __global__ __launch_bounds__(256) void xent_finish_k(int N, int P, const float2*
       nats[row] = nat;
     }
   }
-  if (lane == 0) red[wave] = (row < N) ? nat : 0.0f;
+  float term = nat;
+  if (w && row < N) term = w[row] != 0.0f ? w[row] * nat : 0.0f;
+  if (lane == 0) red[wave] = (row < N) ? term : 0.0f;
   __syncthreads();
   if (threadIdx.x == 0) {
     float t = 0.0f;
@@ -104,12 +107,13 @@ __global__ __launch_bounds__(256) void xent_rows_stats_k(int N, int Vc, int v0, 
 template <typename T>
 __global__ __launch_bounds__(256) void xent_rows_grad_k(int N, int Vc, int v0, const float* __restrict__ z, long ldz,
                                                         const int32_t* __restrict__ tgt, const float* __restrict__ lse,
-                                                        float scale, T* __restrict__ dz, long lddz) {
+                                                        float scale, const float* __restrict__ w, T* __restrict__ dz,
+                                                        long lddz) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)N * Vc) return;
   const int row = (int)(idx / Vc), c = (int)(idx % Vc);
   const float p = expf(z[(long)row * ldz + c] - lse[row]);
-  const float g = (p - (c + v0 == tgt[row] ? 1.0f : 0.0f)) * scale;
+  const float g = (p - (c + v0 == tgt[row] ? 1.0f : 0.0f)) * (w ? scale * w[row] : scale);
   dz[(long)row * lddz + c] = from_f32<T>(g);
 }
 
@@ -158,9 +162,9 @@ __global__ __launch_bounds__(1024) void bpb_k(int N, int V, const float* __restr
 
 int xent_finish_blocks(int N) { return cdiv(N, FINISH_ROWS); }
 
-hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, float* lse, float* nats,
-                              float* loss_part, hipStream_t s) {
-  hipLaunchKernelGGL(xent_finish_k, dim3(xent_finish_blocks(N)), dim3(256), 0, s, N, P, part, ztgt, lse, nats,
+hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, const float* w, float* lse,
+                              float* nats, float* loss_part, hipStream_t s) {
+  hipLaunchKernelGGL(xent_finish_k, dim3(xent_finish_blocks(N)), dim3(256), 0, s, N, P, part, ztgt, w, lse, nats,
                      loss_part);
   return hipGetLastError();
 }
@@ -177,13 +181,13 @@ hipError_t launch_xent_rows_stats(int N, int Vc, int v0, const float* z, long ld
 }
 
 hipError_t launch_xent_rows_grad(int dtype, int N, int Vc, int v0, const float* z, long ldz, const int32_t* tgt,
-                                 const float* lse, float scale, void* dz, long lddz, hipStream_t s) {
+                                 const float* lse, float scale, const float* w, void* dz, long lddz, hipStream_t s) {
   dim3 grid((unsigned)cdiv((long)N * Vc, 256));
   if (dtype == 1)
-    hipLaunchKernelGGL(xent_rows_grad_k<bf16>, grid, dim3(256), 0, s, N, Vc, v0, z, ldz, tgt, lse, scale, (bf16*)dz,
+    hipLaunchKernelGGL(xent_rows_grad_k<bf16>, grid, dim3(256), 0, s, N, Vc, v0, z, ldz, tgt, lse, scale, w, (bf16*)dz,
                        lddz);
   else
-    hipLaunchKernelGGL(xent_rows_grad_k<float>, grid, dim3(256), 0, s, N, Vc, v0, z, ldz, tgt, lse, scale, (float*)dz,
+    hipLaunchKernelGGL(xent_rows_grad_k<float>, grid, dim3(256), 0, s, N, Vc, v0, z, ldz, tgt, lse, scale, w, (float*)dz,
                        lddz);
   return hipGetLastError();
 }

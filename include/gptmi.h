@@ -151,6 +151,22 @@ int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h,
                          void* dh, float* dW, int accumulate,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* lm_head_xent_fwd_bwd with a weight per token ("Train your own ChatGPT",
+ * section 6.3: the chat fine-tuning loss multiplies the per-token losses by
+ * a 0/1 mask of the tokens to learn, sums, and divides by the mask's sum).
+ * token_weight: device fp32 [N].  loss = loss_scale * sum_n w_n nats_n and
+ * row n of the logit gradient carries loss_scale * w_n; a token with w_n = 0
+ * is left out of the sum entirely (its nats are still written, NaN when its
+ * target is out of range).  The masked mean is w = mask, loss_scale =
+ * 1 / sum(mask).  Other arguments, layouts and errors as
+ * lm_head_xent_fwd_bwd, which equals this call with every w_n = 1. */
+int lm_head_xent_weighted_fwd_bwd(const gpt_config* cfg, int N, const void* h,
+                                  const void* W, const int32_t* targets,
+                                  const float* token_weight, float loss_scale,
+                                  float* loss, float* nats, void* dh, float* dW,
+                                  int accumulate, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Bits-per-byte reduction ([nanochat] 6.2, loss_eval.py paragraph): with
  * b_n = token_bytes[targets[n]], adds sum over b_n > 0 of nats[n] into
  * *sum_nats (fp64) and sum of b_n into *sum_bytes (int64).  Tokens with

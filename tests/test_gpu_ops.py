@@ -64,6 +64,51 @@ def test_lm_head_xent(dtype, N, C, V):
     print(dtype, N, C, V, {k: f"{v:.2e}" for k, v in rep.items()})
 
 
+XENT_W = [
+    ("bf16", 517, 768, 50304, "mask"),      # the chat fine-tuning masked mean, ragged chunks
+    ("bf16", 1000, 1280, 32768, "weights"),  # general non-negative weights
+    ("fp32", 200, 64, 9000, "mask"),
+]
+
+
+@pytest.mark.parametrize("dtype,N,C,V,kind", XENT_W)
+def test_lm_head_xent_weighted(dtype, N, C, V, kind):
+    print_case("xent weighted", dtype, N, C, V, kind)
+    rng = np.random.default_rng(3 * N + V)
+    h = synth.round_to(rng.standard_normal((N, C)), dtype)
+    W = synth.round_to(0.05 * rng.standard_normal((V, C)), dtype)
+    y = rng.integers(0, V, N)
+    if kind == "mask":
+        w = (rng.uniform(size=N) < 0.5).astype(np.float64)
+        y[w == 0] = -1          # masked positions may carry an ignore id
+        scale = 1.0 / w.sum()
+    else:
+        w = synth.round_to(rng.uniform(0.0, 2.0, N), "fp32")
+        w[::7] = 0.0
+        scale = 1.0 / N
+    cfg = _cfg(dtype, V, C, H=C // 64 if C >= 64 else 1)
+    c = B.make_config(cfg)
+    ws = workspace(c, 1, N)
+    dh = torch.empty((N, C), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    dW = torch.zeros((V, C), dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nats = torch.zeros(N, dtype=torch.float32, device="cuda")
+    tw = torch.tensor(w, dtype=torch.float32, device="cuda")
+    B.lm_head_xent_weighted_fwd_bwd(c, N, upload(h, dtype), upload(W, dtype), upload_i32(y), tw, scale, loss, nats,
+                                    dh, dW, 0, ws)
+    torch.cuda.synchronize()
+    keep = w != 0
+    y_ref = np.where(keep, y, 0)    # any valid id: a zero-weight row contributes nothing
+    l_ref, n_ref, dh_ref, dW_ref = O.xent_fwd_bwd(h, W, y_ref, scale, weights=w)
+    rep = {}
+    assert_rel("loss", loss.item(), l_ref, REL_LOSS, rep)
+    assert_rel("nats(kept)", to_f64(nats)[keep], n_ref[keep], REL_ACT, rep)
+    assert_rel("dh", to_f64(dh), dh_ref, REL_ACT, rep)
+    assert_rel("dW", to_f64(dW), dW_ref, REL_ACT, rep)
+    assert not to_f64(dh)[~keep].any(), "zero-weight rows must have zero input gradients"
+    print(dtype, N, C, V, kind, {k: f"{v:.2e}" for k, v in rep.items()})
+
+
 def test_xent_uniform_logits_give_ln_V():
     """A zero head weight: every token's nats is ln V."""
     N, C, V = 64, 128, 32768
