@@ -55,6 +55,7 @@ class GPTConfig:
     rope_base: float = 10000.0
     eps: float = 1e-5
     dtype: str = "bf16"          # storage type: "bf16" or "fp32"
+    window: int = 0              # sliding attention window (keys i-W+1..i); 0: full causal
     tied: bool = True            # lm_head weight is wte
     vocab_real: Optional[int] = None  # ids are drawn below this (padded vocab)
 
@@ -263,7 +264,7 @@ def oracle_cfg(cfg: GPTConfig) -> dict:
     return dict(n_layer=cfg.n_layer, n_head=cfg.n_head, n_embd=cfg.n_embd,
                 vocab_size=cfg.vocab_size, norm=cfg.norm, bias=cfg.bias,
                 rope=cfg.rope, qk_norm=cfg.qk_norm, rope_base=cfg.rope_base,
-                eps=cfg.eps)
+                eps=cfg.eps, window=cfg.window)
 
 
 def make_adamw_inputs(shapes, seed: int = 0, g_std: float = 1e-2):

@@ -190,17 +190,29 @@ def linear_bwd(dy, x, w, has_bias):
 # Reading: scores scaled by 1/sqrt(D) in every configuration.
 # ----------------------------------------------------------------------------
 
-def causal_attention_fwd(q, k, v):
+def _hidden(T, window):
+    """Mask of the key positions j a query i does not see: the future j > i,
+    and with a sliding window of W > 0 positions also j <= i - W ("Train your
+    own ChatGPT", 6.2: per-layer (left, right) windows of the "SSSL" pattern;
+    the window lengths are a parameter here, since the pages give none)."""
+    hidden = np.triu(np.ones((T, T), dtype=bool), k=1)
+    if window and window > 0:
+        hidden |= np.tril(np.ones((T, T), dtype=bool), k=-window)
+    return hidden
+
+
+def causal_attention_fwd(q, k, v, window=0):
     """q, k, v: [B, T, H, D].  Returns (O [B,T,H,D], lse [B,H,T]).
 
-    For each (b, h): S = q k^T / sqrt(D), S_ij = -inf for j > i,
-    P = row softmax of S, O = P v.  lse is the row log-sum-exp of S.
+    For each (b, h): S = q k^T / sqrt(D), S_ij = -inf for j > i (and for
+    j <= i - window when window > 0), P = row softmax of S, O = P v.  lse is
+    the row log-sum-exp of S.
     """
     B, T, H, D = q.shape
     scale = 1.0 / math.sqrt(D)
     out = np.empty_like(q)
     lse = np.empty((B, H, T))
-    future = np.triu(np.ones((T, T), dtype=bool), k=1)
+    future = _hidden(T, window)
     for b in range(B):
         for h in range(H):
             S = (q[b, :, h, :] @ k[b, :, h, :].T) * scale
@@ -214,7 +226,7 @@ def causal_attention_fwd(q, k, v):
     return out, lse
 
 
-def causal_attention_bwd(dO, q, k, v):
+def causal_attention_bwd(dO, q, k, v, window=0):
     """Gradients of causal_attention_fwd's O with respect to q, k, v.
 
     With P the masked softmax: dV = P^T dO, dP = dO v^T,
@@ -226,7 +238,7 @@ def causal_attention_bwd(dO, q, k, v):
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    future = np.triu(np.ones((T, T), dtype=bool), k=1)
+    future = _hidden(T, window)
     for b in range(B):
         for h in range(H):
             qb, kb, vb, dob = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], dO[b, :, h, :]
@@ -272,7 +284,7 @@ def block_fwd(cfg, x, p):
     if cfg["qk_norm"]:
         q_n, _ = rmsnorm_fwd(q_r, cfg["eps"])
         k_n, _ = rmsnorm_fwd(k_r, cfg["eps"])
-    o, lse = causal_attention_fwd(q_n, k_n, v)
+    o, lse = causal_attention_fwd(q_n, k_n, v, cfg.get("window", 0))
     o = o.reshape(x.shape)
     x1 = x + linear_fwd(o, p["w_o"], p.get("b_o") if bias else None)
     a2 = norm_fwd(cfg, x1, p.get("ln2_w"), p.get("ln2_b"))
@@ -298,7 +310,8 @@ def block_bwd(cfg, dy, cache, p):
     dx1 = dy + dn2
     # attention: x1 = x + attn(a1) W_o^T + b_o
     do, grads["w_o"], grads["b_o"] = linear_bwd(dx1, cache["o"], p["w_o"], bias)
-    dq_n, dk_n, dv = causal_attention_bwd(_heads(do, H), cache["q_n"], cache["k_n"], cache["v"])
+    dq_n, dk_n, dv = causal_attention_bwd(_heads(do, H), cache["q_n"], cache["k_n"], cache["v"],
+                                          cfg.get("window", 0))
     dq_r, dk_r = dq_n, dk_n
     if cfg["qk_norm"]:
         dq_r = rmsnorm_bwd(dq_n, cache["q_r"], cfg["eps"])

@@ -332,3 +332,45 @@ def test_zipf_head_frequency():
     p0 = 1.0 / (k ** -1.1).sum()
     assert abs((ids == 0).mean() - p0) < 0.005
     assert ids.min() >= 0 and ids.max() < 50257
+
+
+# ---- sliding-window attention --------------------------------------------------
+
+@pytest.mark.parametrize("window", [1, 2, 4])
+def test_windowed_attention_brute_force(window):
+    """Query i attends to keys max(0, i - W + 1) .. i only."""
+    rng = np.random.default_rng(60 + window)
+    B, T, H, D = 1, 7, 2, 3
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    o, lse = O.causal_attention_fwd(q, k, v, window)
+    for h in range(H):
+        for i in range(T):
+            js = range(max(0, i - window + 1), i + 1)
+            s = {j: sum(q[0, i, h, d] * k[0, j, h, d] for d in range(D)) / math.sqrt(D) for j in js}
+            den = sum(math.exp(x) for x in s.values())
+            assert abs(lse[0, h, i] - math.log(den)) < 1e-12
+            for d in range(D):
+                ref = sum(math.exp(s[j]) / den * v[0, j, h, d] for j in js)
+                assert abs(o[0, i, h, d] - ref) < 1e-12
+
+
+def test_window_one_is_v_and_wide_window_is_causal():
+    rng = np.random.default_rng(70)
+    q, k, v = (rng.standard_normal((2, 10, 2, 4)) for _ in range(3))
+    o1, _ = O.causal_attention_fwd(q, k, v, 1)
+    np.testing.assert_allclose(o1, v, atol=1e-15)
+    ofull, lfull = O.causal_attention_fwd(q, k, v)
+    for w in (10, 11, 100):
+        ow, lw = O.causal_attention_fwd(q, k, v, w)
+        np.testing.assert_array_equal(ow, ofull)
+        np.testing.assert_array_equal(lw, lfull)
+
+
+def test_window_zero_q_is_trailing_mean():
+    rng = np.random.default_rng(71)
+    T, W = 9, 3
+    k, v = rng.standard_normal((1, T, 1, 4)), rng.standard_normal((1, T, 1, 4))
+    o, _ = O.causal_attention_fwd(np.zeros_like(k), k, v, W)
+    for i in range(T):
+        ref = v[0, max(0, i - W + 1):i + 1, 0].mean(axis=0)
+        np.testing.assert_allclose(o[0, i, 0], ref, atol=1e-14)

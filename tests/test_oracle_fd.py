@@ -190,3 +190,14 @@ def test_xent_weighted_fd():
     _check(lambda t: O.xent_fwd_bwd(t, W, y, 0.37, want_grad=False, weights=w)[0], h, dh, rng)
     _check(lambda t: O.xent_fwd_bwd(h, t, y, 0.37, want_grad=False, weights=w)[0], W, dW, rng)
     assert not dh[3].any()
+
+
+@pytest.mark.parametrize("window", [1, 3])
+def test_windowed_attention_bwd_fd(window):
+    rng = np.random.default_rng(40 + window)
+    q, k, v = (rng.standard_normal((2, 9, 2, 8)) for _ in range(3))
+    R = rng.standard_normal(q.shape)
+    dq, dk, dv = O.causal_attention_bwd(R, q, k, v, window)
+    _check(lambda t: (O.causal_attention_fwd(t, k, v, window)[0] * R).sum(), q, dq, rng)
+    _check(lambda t: (O.causal_attention_fwd(q, t, v, window)[0] * R).sum(), k, dk, rng)
+    _check(lambda t: (O.causal_attention_fwd(q, k, t, window)[0] * R).sum(), v, dv, rng)
