@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time the GPT-2 block, GPT-2 step and d20 eval")
     ap.add_argument("--adamw", action="store_true",
                     help="also time the AdamW step over the d20 model's parameter set (HBM-bound)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="also time the d20 block with sliding-window attention of this many keys")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
@@ -230,12 +232,47 @@ def main():
         "roofline": roof,
         "kernels": sites,
     }
-    if args.extra or args.adamw:
+    if args.extra or args.adamw or args.window:
         out["extra"] = extra_workloads(args) if args.extra else {}
-        out["extra"]["adamw_d20_model"] = adamw_workload(args)
+        if args.adamw:
+            out["extra"]["adamw_d20_model"] = adamw_workload(args)
+        if args.window:
+            out["extra"][f"d20_block_window{args.window}"] = window_workload(args, args.window)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def window_workload(args, window):
+    """The d20 block fwd+bwd with sliding-window attention: query i attends
+    to keys i - window + 1 .. i.  Useful attention work is 12 D FLOP per
+    visible (query, key) pair and (batch, head): Q K^T and P V forward (4 D),
+    dV, dP, dK and dQ backward (8 D); with a window that covers the sequence
+    this is the causal block's 6 B H D T^2."""
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import BlockRunner
+    w = synth.scaled(synth.D20_BLOCK, window=window)
+    cfg = w.cfg
+    x, dy, p = synth.make_block_inputs(w)
+    r = BlockRunner(cfg, w.B, w.T, x, dy, p)
+    ms = time_steps(r.step, args.steps, args.warmup)
+    B.gpt_trace_begin(64 * args.steps)
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    trace = B.gpt_trace_end()
+    T, C, H = w.T, cfg.n_embd, cfg.n_head
+    D = C // H
+    pairs = sum(min(i + 1, window) for i in range(T))   # visible (query, key) pairs per (b, h)
+    attn = 12.0 * w.B * H * D * pairs                    # 4 D (fwd) + 8 D (bwd) FLOP per pair
+    flops = 72.0 * C * C * w.B * T + attn
+    del r
+    torch.cuda.empty_cache()
+    return {"window": window, "ms": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
+            "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16,
+            "attn_us": {k: round(v[1] / v[0], 2) for k, v in trace.items() if k.startswith("attn")}}
 
 
 def adamw_workload(args):

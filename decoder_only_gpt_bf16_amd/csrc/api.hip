@@ -102,6 +102,7 @@ int check_cfg(const gpt_config* cfg, Dims& d) {
   if (cfg->norm != GPT_NORM_LAYERNORM && cfg->norm != GPT_NORM_RMSNORM)
     return fail(GPT_ERR_INVALID, "unknown norm %d", cfg->norm);
   if (!(cfg->norm_eps >= 0.0f)) return fail(GPT_ERR_INVALID, "norm_eps must be >= 0");
+  if (cfg->attn_window < 0) return fail(GPT_ERR_INVALID, "attn_window must be >= 0");
   d.C = cfg->n_embd;
   d.H = cfg->n_head;
   d.D = d.C / d.H;
@@ -432,7 +433,7 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   RUN("qkv_gemm", launch_gemm(g, ty, nullptr, s));
   if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
-  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, sv.qkv, sv.o, sv.lse, s));
+  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, cfg->attn_window, sv.qkv, sv.o, sv.lse, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
   g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
   RUN("out_gemm", launch_gemm(g, ty, nullptr, s));
@@ -515,12 +516,16 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   const QkBwd qk{cfg->rope, cfg->qk_norm, N, sv.cs, sv.qkr};
   if (attn_mfma_supported(ty, d.D)) {
     // dQ pass first (it also forms delta); QK-norm / RoPE backward in both stores
-    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
-    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, cfg->attn_window, sv.qkv, sv.o, b.dO, sv.lse, b.delta,
+                                          b.dqkv, qk, s));
+    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, cfg->attn_window, sv.qkv, b.dO, sv.lse, b.delta,
+                                              b.dqkv, qk, s));
   } else {
     RUN("attn_delta", launch_attn_delta(ty, B, T, d.H, d.D, sv.o, b.dO, b.delta, s));
-    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, sv.qkv, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
-    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, sv.qkv, sv.o, b.dO, sv.lse, b.delta, b.dqkv, qk, s));
+    RUN("attn_bwd_dkdv", launch_attn_bwd_dkdv(ty, B, T, d.H, d.D, cfg->attn_window, sv.qkv, b.dO, sv.lse, b.delta,
+                                              b.dqkv, qk, s));
+    RUN("attn_bwd_dq", launch_attn_bwd_dq(ty, B, T, d.H, d.D, cfg->attn_window, sv.qkv, sv.o, b.dO, sv.lse, b.delta,
+                                          b.dqkv, qk, s));
     if (cfg->rope || cfg->qk_norm)
       RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, sv.cs, sv.qkv, sv.qkr, b.dqkv, s));
   }

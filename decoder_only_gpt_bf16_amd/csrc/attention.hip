@@ -228,7 +228,7 @@ __device__ __forceinline__ void attn_block(int T, int H, int& rank, int& h, int&
 template <int D, bool FIXED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                         bf16* __restrict__ o, float* __restrict__ lse,
-                                                        float scale_log2, float shift_log2) {
+                                                        float scale_log2, float shift_log2, int W) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
@@ -264,8 +264,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D>::direct(sK[0], rK, ld, 0, T);
-  RowTile<D>::direct(sV[0], rV, ld, 0, T);
+  // with a window of W keys, query i sees keys i - W + 1 .. i: the block's
+  // first tile is the one holding key q0 - W + 1
+  const int t_first = W > 0 ? max(0, q0 - W + 1) / 64 : 0;
+  RowTile<D>::direct(sK[0], rK, ld, 64 * t_first, T);
+  RowTile<D>::direct(sV[0], rV, ld, 64 * t_first, T);
   wait_lds_loads();
   __syncthreads();
 
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
       RowTile<D>::direct(sK[cur ^ 1], rK, ld, kv0 + 64, T);
       RowTile<D>::direct(sV[cur ^ 1], rV, ld, kv0 + 64, T);
     }
-    if (kv0 <= qw + 31 && qw < T) {
+    if (kv0 <= qw + 31 && qw < T && (W == 0 || kv0 + 63 > qw - W)) {
       // S^T = K Q^T for two 32-key sub-tiles; k-step s+1 fragments are read
       // while the MFMAs of step s run
       f32x16 st[2];
@@ -314,14 +317,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
             float x = st[jt][r];
             if constexpr (decltype(masked)::value) {
               const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (j > qi || j >= T) x = -INFINITY;
+              if (j > qi || j >= T || (W > 0 && j <= qi - W)) x = -INFINITY;
             }
             p[jt][r] = x;
             mx = fmaxf(mx, x);
           }
         return mx;
       };
-      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T);
+      const bool need_mask = (kv0 + 63 > qw) || (kv0 + 64 > T) || (W > 0 && kv0 <= qw + 31 - W);
       float mx = need_mask ? scores(std::true_type{}) : scores(std::false_type{});
       float m_new = m_run, msub = m_run;
       bool dead = false;
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16
     wait_lds_loads();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_first; t < ntiles; t += 2) {
     tile(t, std::integral_constant<int, 0>{});
     if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(int T, int H, const
                                                              const float* __restrict__ lse,
                                                              const float* __restrict__ delta,
                                                              bf16* __restrict__ dqkv, float scale_log2,
-                                                             float scale, QkBwd qk) {
+                                                             float scale, QkBwd qk, int W) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   constexpr int NCP = 2 * (64 * KU / 512);  // tile copies per wave (Q and dO)
   __shared__ uint4 sQ[3][64 * KU];
@@ -528,7 +531,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(int T, int H, const
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
 
   const int t_begin = k0 / 64;
-  const int t_end = (T + 63) / 64;
+  // with a window of W keys the last query that sees key k0 + 127 is
+  // k0 + 126 + W
+  const int t_end = W > 0 ? (min(T - 1, k0 + 126 + W) / 64) + 1 : (T + 63) / 64;
   // Q and dO tiles by all 8 waves; every wave also copies the tile's 64
   // log-sum-exp and delta values (4 bytes a lane, the same bytes to the same
   // place), so that all waves issue the same number of copies and the wait
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(int T, int H, const
           float x = __builtin_amdgcn_exp2f(fmaf(S[4 * g + e], scale_log2, -Ls[e]));
           if constexpr (decltype(masked)::value) {
             const int qi = q0h + 8 * g + 4 * hf + e;
-            if (qi < kj || qi >= T || kj >= T) x = 0.0f;
+            if (qi < kj || qi >= T || kj >= T || (W > 0 && qi - W >= kj)) x = 0.0f;
           }
           pv[e] = x;
           dv4[e] = x * (dPs[e] - Ds[e]);
@@ -597,7 +602,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(int T, int H, const
         dw[2 * g + 1] = pack2(dv4[2], dv4[3]);
       }
     };
-    if ((q0h < kw + 31) || (q0h + 32 > T) || (kw + 32 > T)) probs(std::true_type{});
+    if ((q0h < kw + 31) || (q0h + 32 > T) || (kw + 32 > T) || (W > 0 && q0h + 31 - W >= kw)) probs(std::true_type{});
     else probs(std::false_type{});
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ delta,
                                                            bf16* __restrict__ dqkv, float scale_log2,
-                                                           float scale, QkBwd qk) {
+                                                           float scale, QkBwd qk, int W) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
@@ -773,8 +778,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
 
   const int kv_end = min(T, q0 + 128);
   const int ntiles = (kv_end + 63) / 64;
-  RowTile<D>::direct(sK[0], rK, ld, 0, T);
-  RowTile<D>::direct(sV[0], rV, ld, 0, T);
+  const int t_first = W > 0 ? max(0, q0 - W + 1) / 64 : 0;  // as in the forward
+  RowTile<D>::direct(sK[0], rK, ld, 64 * t_first, T);
+  RowTile<D>::direct(sV[0], rV, ld, 64 * t_first, T);
   wait_lds_loads();
   __syncthreads();
   // the loop is unrolled by two so that every LDS buffer index is a
@@ -788,13 +794,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
       RowTile<D>::direct(sK[cur ^ 1], rK, ld, kv0 + 64, T);
       RowTile<D>::direct(sV[cur ^ 1], rV, ld, kv0 + 64, T);
     }
-    if (kv0 <= qw + 31 && qw < T) {
+    if (kv0 <= qw + 31 && qw < T && (W == 0 || kv0 + 63 > qw - W)) {
       // the 64-key tile is processed as two 32-key halves: S^T = K Q^T and
       // dP^T = V dO^T for the half, dS^T, then dQ^T += K^T dS^T over it;
       // only one half's scores are live at a time
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        if (kv0 + 32 * jt > qw + 31) break;  // half above the diagonal
+        if (kv0 + 32 * jt > qw + 31) break;                        // half above the diagonal
+        if (W > 0 && kv0 + 32 * jt + 31 <= qw - W) continue;       // half left of the window
         f32x16 St, dPt;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { St[r] = 0.0f; dPt[r] = 0.0f; }
@@ -811,13 +818,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
             float pv = __builtin_amdgcn_exp2f(fmaf(St[r], scale_log2, -L2));
             if constexpr (decltype(masked)::value) {
               const int j = kv0 + 32 * jt + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (j > qi || j >= T || qi >= T) pv = 0.0f;
+              if (j > qi || j >= T || qi >= T || (W > 0 && j <= qi - W)) pv = 0.0f;
             }
             ds[r] = pv * (dPt[r] - Dl);
           }
         };
         const int k0 = kv0 + 32 * jt;
-        if ((k0 + 31 > qw) || (k0 + 32 > T) || (qw + 32 > T)) grads(std::true_type{});
+        if ((k0 + 31 > qw) || (k0 + 32 > T) || (qw + 32 > T) || (W > 0 && k0 <= qw + 31 - W))
+          grads(std::true_type{});
         else grads(std::false_type{});
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -832,7 +840,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
     wait_lds_loads();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_first; t < ntiles; t += 2) {
     tile(t, std::integral_constant<int, 0>{});
     if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
@@ -866,7 +874,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(int T, int H, const b
 // One thread per query (forward, dQ) or per key (dK, dV); fp32 arithmetic.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_fwd_simt(int TT, int H, const T* __restrict__ qkv, T* __restrict__ o,
-                                                    float* __restrict__ lse, float scale) {
+                                                    float* __restrict__ lse, float scale, int W) {
   const int qi = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (qi >= TT) return;
@@ -876,7 +884,7 @@ __global__ __launch_bounds__(64) void attn_fwd_simt(int TT, int H, const T* __re
   float q[D], acc[D];
   for (int d = 0; d < D; ++d) { q[d] = to_f32(base[(long)qi * ld + d]) * scale; acc[d] = 0.0f; }
   float m = -INFINITY, l = 0.0f;
-  for (int j = 0; j <= qi; ++j) {
+  for (int j = W > 0 ? max(0, qi - W + 1) : 0; j <= qi; ++j) {
     const T* kr = base + (long)j * ld + C;
     float s = 0.0f;
     for (int d = 0; d < D; ++d) s = fmaf(q[d], to_f32(kr[d]), s);
@@ -897,7 +905,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_bwd_dq_simt(int TT, int H, const T* __restrict__ qkv,
                                                        const T* __restrict__ dO, const float* __restrict__ lse,
                                                        const float* __restrict__ delta, T* __restrict__ dqkv,
-                                                       float scale) {
+                                                       float scale, int W) {
   const int qi = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (qi >= TT) return;
@@ -909,7 +917,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_simt(int TT, int H, const T* _
   for (int d = 0; d < D; ++d) { q[d] = to_f32(base[(long)qi * ld + d]); g[d] = to_f32(dob[d]); acc[d] = 0.0f; }
   const long rl = ((long)b * H + h) * TT + qi;
   const float L = lse[rl], Dl = delta[rl];
-  for (int j = 0; j <= qi; ++j) {
+  for (int j = W > 0 ? max(0, qi - W + 1) : 0; j <= qi; ++j) {
     const T* kr = base + (long)j * ld + C;
     const T* vr = kr + C;
     float s = 0.0f, dp = 0.0f;
@@ -926,7 +934,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_bwd_dkdv_simt(int TT, int H, const T* __restrict__ qkv,
                                                          const T* __restrict__ dO, const float* __restrict__ lse,
                                                          const float* __restrict__ delta, T* __restrict__ dqkv,
-                                                         float scale) {
+                                                         float scale, int W) {
   const int kj = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (kj >= TT) return;
@@ -939,7 +947,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simt(int TT, int H, const T*
     v[d] = to_f32(base[(long)kj * ld + 2 * C + d]);
     dk[d] = 0.0f; dv[d] = 0.0f;
   }
-  for (int i = kj; i < TT; ++i) {
+  const int i_end = W > 0 ? min(TT, kj + W) : TT;
+  for (int i = kj; i < i_end; ++i) {
     const T* qr = base + (long)i * ld;
     const T* gr = dO + ((long)b * TT + i) * C + h * D;
     const long rl = ((long)b * H + h) * TT + i;
@@ -1070,28 +1079,28 @@ __global__ __launch_bounds__(256) void delta_k(int N, int TT, int H, int D, cons
 
 template <typename T, int D>
 hipError_t simt_all(int which, int B, int TT, int H, const void* qkv, const void* dO, void* out, float* lse,
-                    const float* delta, hipStream_t s) {
+                    const float* delta, int W, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)D);
   dim3 grid(cdiv(TT, 64), H, B);
   if (which == 0)
-    hipLaunchKernelGGL((attn_fwd_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (T*)out, lse, scale);
+    hipLaunchKernelGGL((attn_fwd_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (T*)out, lse, scale, W);
   else if (which == 1)
     hipLaunchKernelGGL((attn_bwd_dq_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (const T*)dO, lse,
-                       delta, (T*)out, scale);
+                       delta, (T*)out, scale, W);
   else
     hipLaunchKernelGGL((attn_bwd_dkdv_simt<T, D>), grid, dim3(64), 0, s, TT, H, (const T*)qkv, (const T*)dO, lse,
-                       delta, (T*)out, scale);
+                       delta, (T*)out, scale, W);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t simt_dispatch(int which, int B, int TT, int H, int D, const void* qkv, const void* dO, void* out,
-                         float* lse, const float* delta, hipStream_t s) {
+                         float* lse, const float* delta, int W, hipStream_t s) {
   switch (D) {
-    case 16: return simt_all<T, 16>(which, B, TT, H, qkv, dO, out, lse, delta, s);
-    case 32: return simt_all<T, 32>(which, B, TT, H, qkv, dO, out, lse, delta, s);
-    case 64: return simt_all<T, 64>(which, B, TT, H, qkv, dO, out, lse, delta, s);
-    case 128: return simt_all<T, 128>(which, B, TT, H, qkv, dO, out, lse, delta, s);
+    case 16: return simt_all<T, 16>(which, B, TT, H, qkv, dO, out, lse, delta, W, s);
+    case 32: return simt_all<T, 32>(which, B, TT, H, qkv, dO, out, lse, delta, W, s);
+    case 64: return simt_all<T, 64>(which, B, TT, H, qkv, dO, out, lse, delta, W, s);
+    case 128: return simt_all<T, 128>(which, B, TT, H, qkv, dO, out, lse, delta, W, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1132,8 +1141,9 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, const void* qkv, void* o,
-                           float* lse, hipStream_t s) {
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, int window, const void* qkv,
+                           void* o, float* lse, hipStream_t s) {
+  const int W = window >= T ? 0 : window;  // a window of T or more keys is the full causal mask
   if (attn_mfma_supported(dtype, D)) {
     const float scale_log2 = LOG2E / sqrtf((float)D);
     // with QK-norm |q|, |k| <= sqrt(D) (up to bf16 rounding), so a scaled
@@ -1141,7 +1151,7 @@ hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, c
     const float shift_log2 = 1.03f * sqrtf((float)D) * LOG2E;
     dim3 grid(cdiv(T, 128) * H * B);
 #define AF(DD, FX) hipLaunchKernelGGL((attn_fwd_mfma<DD, FX>), grid, dim3(256), 0, s, T, H, (const bf16*)qkv, \
-                                      (bf16*)o, lse, scale_log2, shift_log2)
+                                      (bf16*)o, lse, scale_log2, shift_log2, W)
     if (D == 128) {
       if (qk_norm) AF(128, true); else AF(128, false);
     } else {
@@ -1150,8 +1160,8 @@ hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, c
 #undef AF
     return hipGetLastError();
   }
-  if (dtype == 1) return simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, s);
-  return simt_dispatch<float>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, s);
+  if (dtype == 1) return simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s);
+  return simt_dispatch<float>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s);
 }
 
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO, float* delta,
@@ -1165,38 +1175,41 @@ hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, int window, const void* qkv, const void* dO,
                                 const float* lse, const float* delta, void* dqkv, const QkBwd& qk, hipStream_t s) {
+  const int W = window >= T ? 0 : window;
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
     dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_bwd_dkdv_mfma<128>, g, dim3(512), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale, qk);
+                         delta, (bf16*)dqkv, scale_log2, scale, qk, W);
     else
       hipLaunchKernelGGL(attn_bwd_dkdv_mfma<64>, g, dim3(512), 0, s, T, H, (const bf16*)qkv, (const bf16*)dO, lse,
-                         delta, (bf16*)dqkv, scale_log2, scale, qk);
+                         delta, (bf16*)dqkv, scale_log2, scale, qk, W);
     return hipGetLastError();
   }
-  if (dtype == 1) return simt_dispatch<bf16>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
-  return simt_dispatch<float>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+  if (dtype == 1) return simt_dispatch<bf16>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, W, s);
+  return simt_dispatch<float>(2, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, W, s);
 }
 
-hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* o, const void* dO,
-                              const float* lse, float* delta, void* dqkv, const QkBwd& qk, hipStream_t s) {
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, int window, const void* qkv, const void* o,
+                              const void* dO, const float* lse, float* delta, void* dqkv, const QkBwd& qk,
+                              hipStream_t s) {
+  const int W = window >= T ? 0 : window;
   if (attn_mfma_supported(dtype, D)) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
     dim3 g(cdiv(T, 128) * H * B);
     if (D == 128)
       hipLaunchKernelGGL(attn_bwd_dq_mfma<128>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk);
+                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk, W);
     else
       hipLaunchKernelGGL(attn_bwd_dq_mfma<64>, g, dim3(256), 0, s, T, H, (const bf16*)qkv, (const bf16*)o,
-                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk);
+                         (const bf16*)dO, lse, delta, (bf16*)dqkv, scale_log2, scale, qk, W);
     return hipGetLastError();
   }
-  if (dtype == 1) return simt_dispatch<bf16>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
-  return simt_dispatch<float>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, s);
+  if (dtype == 1) return simt_dispatch<bf16>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, W, s);
+  return simt_dispatch<float>(1, B, T, H, D, qkv, dO, dqkv, (float*)lse, delta, W, s);
 }

@@ -142,7 +142,8 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
 // Causal attention forward: q, k, v inside qkv [N, 3C]; o [N, C]; lse fp32 [B, H, T].
 // qk_norm != 0 promises RMS-normalised q and k (|q|, |k| <= sqrt(D)), which
 // lets the softmax use a fixed shift instead of a running maximum.
-hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, const void* qkv, void* o,
+// window > 0: query i attends to keys i - window + 1 .. i only (0: full causal).
+hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, int window, const void* qkv, void* o,
                            float* lse, hipStream_t s);
 // delta[b, h, t] = sum_d dO * O (fp32 [B, H, T]).
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO,
@@ -159,9 +160,10 @@ struct QkBwd {
 // the dK/dV pass, and both apply the QK-norm / RoPE backward of qk.  Other
 // paths: delta comes from launch_attn_delta, qk is ignored and
 // launch_qk_bwd follows.
-hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, const void* qkv, const void* dO,
+hipError_t launch_attn_bwd_dkdv(int dtype, int B, int T, int H, int D, int window, const void* qkv, const void* dO,
                                 const float* lse, const float* delta, void* dqkv, const QkBwd& qk, hipStream_t s);
-hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, const void* qkv, const void* o, const void* dO,
+hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, int window, const void* qkv, const void* o,
+                              const void* dO,
                               const float* lse, float* delta, void* dqkv, const QkBwd& qk, hipStream_t s);
 bool attn_mfma_supported(int dtype, int D);
 

@@ -75,6 +75,11 @@ typedef struct gpt_config {
   float   rope_base;
   float   norm_eps;    /* eps of every norm (LayerNorm, RMSNorm, QK-norm) */
   int32_t dtype;       /* GPT_DTYPE_BF16 or GPT_DTYPE_FP32 storage        */
+  int32_t attn_window; /* 0: causal attention over all earlier positions;
+                          W > 0: position i attends to i-W+1 .. i only (the
+                          sliding windows of the "SSSL" layer pattern,
+                          [nanochat] 6.2; per-layer windows are per-call
+                          configs).  W >= T is the full causal mask.      */
 } gpt_config;
 
 /* Block parameters (device pointers, storage dtype).  Absent ones are NULL:

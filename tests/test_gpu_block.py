@@ -24,12 +24,21 @@ CASES = [
     ("d20_block", dict(B=1, T=64), False),
     ("gpt2_block", dict(), False),   # full: B=8, T=1024
     ("d20_block", dict(), False),    # full: B=4, T=2048 (the benchmarked workload)
+    # sliding-window attention: windows that cut tiles, a window of one key,
+    # the 64-wide heads, the fp32 (SIMT) path, and the full d20 size
+    ("d20_block", dict(B=2, T=320, window=96), False),
+    ("d20_block", dict(B=2, T=320, window=200), False),
+    ("d20_block", dict(B=1, T=300, window=1), False),
+    ("gpt2_block", dict(B=2, T=200, window=64), True),
+    ("tiny_gpt_fp32", dict(B=2, T=32, window=5), False),
+    ("d20_block", dict(window=512), False),
 ]
 
 
 def _ids(c):
     name, sz, aff = c
-    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{'-affine' if aff else ''}"
+    win = f"-W{sz['window']}" if "window" in sz else ""
+    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{win}{'-affine' if aff else ''}"
 
 
 def _run(w, random_affine, seed=0):
@@ -44,7 +53,7 @@ def _run(w, random_affine, seed=0):
 def test_block_parity(case):
     name, sz, aff = case
     w = synth.scaled(synth.BY_NAME[name], **sz)
-    print_case("block", name, w.B, w.T, "affine" if aff else "")
+    print_case("block", name, w.B, w.T, f"window={w.cfg.window}", "affine" if aff else "")
     x, dy, p, r = _run(w, aff)
     cfg = synth.oracle_cfg(w.cfg)
     y_ref, cache = O.block_fwd(cfg, x, p)
@@ -87,6 +96,28 @@ def test_block_deterministic_and_causal(name):
     yb = r2.y.view(w.B, w.T, -1)
     assert torch.equal(ya[:, : t + 1], yb[:, : t + 1])
     assert not torch.equal(ya[:, t + 1:], yb[:, t + 1:])
+
+
+@pytest.mark.parametrize("name,window", [("d20_block", 70), ("gpt2_block", 130)])
+def test_block_window_locality(name, window):
+    """Bitwise: with a window of W keys, changing the inputs at positions
+    <= t - W leaves the forward output at positions >= t unchanged."""
+    w = synth.scaled(synth.BY_NAME[name], B=2, T=320, window=window)
+    print_case("block-window-locality", name, window)
+    x, dy, p = synth.make_block_inputs(w)
+    r1 = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
+    r1.forward()
+    t = 250
+    x2 = x.copy()
+    x2[:, : t - window + 1] = synth.round_to(np.random.default_rng(5).standard_normal(x2[:, : t - window + 1].shape),
+                                             "bf16")
+    r2 = BlockRunner(w.cfg, w.B, w.T, x2, dy, p)
+    r2.forward()
+    torch.cuda.synchronize()
+    ya = r1.y.view(w.B, w.T, -1)
+    yb = r2.y.view(w.B, w.T, -1)
+    assert torch.equal(ya[:, t:], yb[:, t:])
+    assert not torch.equal(ya[:, t - 1], yb[:, t - 1])
 
 
 def test_block_accumulate():
