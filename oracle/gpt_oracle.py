@@ -30,6 +30,7 @@ __all__ = [
     "block_fwd", "block_bwd", "embed_fwd", "embed_bwd",
     "xent_fwd_bwd", "val_bpb", "model_fwd_bwd", "model_eval_nats",
     "norm_fwd", "norm_bwd", "clip_scale", "adamw_step",
+    "FP8_FORMATS", "fp8_round", "fp8_encode", "fp8_quantize", "fp8_gemm",
 ]
 
 
@@ -509,3 +510,61 @@ def adamw_step(p, g, m, v, step, lr, beta1, beta2, eps, weight_decay, decay, sca
     p_new = p * (1.0 - lr * weight_decay) if decay else np.array(p, dtype=np.float64, copy=True)
     p_new = p_new - lr * m_hat / (np.sqrt(v_hat) + eps)
     return p_new, m_new, v_new
+
+
+# ----------------------------------------------------------------------------
+# FP8 GEMMs.  "Train your own ChatGPT", 6.2 (the FP8 paragraph) and the
+# nanochat-d20 card (Pretraining row: the published run trained in FP8): the
+# matmuls run on 8-bit floats with a dynamic per-tensor scale.  The formats
+# are the OCP 8-bit floats: E4M3 (bias 7, no infinities, largest 448) for
+# activations and weights, E5M2 (bias 15, largest 57344) for gradients.
+# Readings: the scale of a tensor is fmt_max / amax (1 when amax = 0), both in
+# float32, and a value's code is x * scale rounded in float32, clamped to
+# +-fmt_max, then rounded to nearest even on the format's grid; the GEMM
+# result is (sum_k qa qb) / (scale_a scale_b).
+# ----------------------------------------------------------------------------
+
+FP8_FORMATS = {"e4m3": dict(mbits=3, bias=7, max=448.0), "e5m2": dict(mbits=2, bias=15, max=57344.0)}
+
+
+def fp8_round(x, fmt):
+    """Nearest value of the format's grid (ties to even), saturating at the
+    largest finite value.  x: float64 array of values to round."""
+    f = FP8_FORMATS[fmt]
+    x = np.clip(np.asarray(x, dtype=np.float64), -f["max"], f["max"])
+    a = np.abs(x)
+    emin = 1 - f["bias"]                       # exponent of the smallest normal
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)                    # subnormals share the quantum of emin
+    q = np.exp2(e - f["mbits"])                # spacing of the grid at a
+    r = np.round(a / q) * q                    # numpy rounds half to even
+    return np.copysign(np.minimum(r, f["max"]), x)
+
+
+def fp8_encode(v, fmt):
+    """Byte codes (uint8) of values already on the format's grid."""
+    f = FP8_FORMATS[fmt]
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    emin = 1 - f["bias"]
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    normal = (a >= 2.0 ** emin) & (a > 0)
+    exp_field = np.where(normal, e + f["bias"], 0)
+    mant = np.where(normal, a / np.exp2(e) - 1.0, a / 2.0 ** emin) * 2 ** f["mbits"]
+    code = (exp_field.astype(np.int64) << f["mbits"]) | np.rint(mant).astype(np.int64)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def fp8_quantize(x, fmt):
+    """(values on the fp8 grid, scale, amax) of a tensor, the scale and the
+    product x * scale formed in float32 as the kernels do."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    scale = np.float32(FP8_FORMATS[fmt]["max"]) / amax if amax > 0 else np.float32(1.0)
+    y = (x32 * scale).astype(np.float64)
+    return fp8_round(y, fmt), float(scale), float(amax)
+
+
+def fp8_gemm(qa, scale_a, qb, scale_b):
+    """C[m, n] = sum_k qa[m, k] qb[n, k] / (scale_a scale_b) in float64."""
+    return (np.asarray(qa, dtype=np.float64) @ np.asarray(qb, dtype=np.float64).T) / (scale_a * scale_b)
