@@ -76,6 +76,10 @@ _SIGS = {
     "gpt_norm_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
     "gpt_adamw_step": (_I, [ctypes.POINTER(AdamwConfigC), _ATP, _I, _VP, _VP, _SZ, _VP]),
     "gpt_adamw_workspace_bytes": (_SZ, [_ATP, _I]),
+    "gpt_fp8_quantize": (_I, [ctypes.c_int64, _VP, _I, _VP, _VP, _VP, _SZ, _VP]),
+    "gpt_fp8_workspace_bytes": (_SZ, [ctypes.c_int64]),
+    "gpt_fp8_gemm": (_I, [_I, _I, _I, _VP, ctypes.c_int64, _I, _VP, _VP, ctypes.c_int64, _I, _VP, _VP,
+                          ctypes.c_int64, _VP]),
     "gpt_trace_begin": (_I, [_I]),
     "gpt_trace_end": (_I, [ctypes.c_char_p, _SZ]),
     "gpt_status_string": (ctypes.c_char_p, [_I]),
@@ -272,3 +276,30 @@ def gpt_adamw_step(tensors, lr, beta1, beta2, eps, weight_decay, step, max_norm,
     cfg = AdamwConfigC(lr, beta1, beta2, eps, weight_decay, int(step), max_norm)
     _check(lib().gpt_adamw_step(ctypes.byref(cfg), arr, len(arr), _p(grad_norm, "f32"), _p(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+FP8_E4M3, FP8_E5M2 = 0, 1
+
+
+def gpt_fp8_workspace_bytes(n: int) -> int:
+    return lib().gpt_fp8_workspace_bytes(int(n))
+
+
+def gpt_fp8_quantize(x, fmt, q, scale, ws, stream=None):
+    """x: bf16 tensor; q: uint8 tensor of x.numel(); scale: fp32 tensor of >= 3."""
+    import torch
+    if x.dtype != torch.bfloat16 or q.dtype != torch.uint8 or q.numel() != x.numel():
+        raise TypeError("x must be bf16 and q a uint8 tensor of the same size")
+    _check(lib().gpt_fp8_quantize(x.numel(), _p(x), int(fmt), _p(q), _p(scale, "f32"), _p(ws), _nbytes(ws),
+                                  _stream(stream)))
+
+
+def gpt_fp8_gemm(qa, fmt_a, scale_a, qb, fmt_b, scale_b, out, stream=None):
+    """qa [M, K], qb [N, K] uint8 codes (row-major); out bf16 [M, N]."""
+    import torch
+    M, K = qa.shape
+    N, K2 = qb.shape
+    if K != K2 or out.shape != (M, N) or out.dtype != torch.bfloat16:
+        raise ValueError("shapes: qa [M, K], qb [N, K], out bf16 [M, N]")
+    _check(lib().gpt_fp8_gemm(M, N, K, _p(qa), qa.stride(0), int(fmt_a), _p(scale_a, "f32"), _p(qb), qb.stride(0),
+                              int(fmt_b), _p(scale_b, "f32"), _p(out), out.stride(0), _stream(stream)))

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgptmi.so")
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "norm.hip", "embed.hip", "xent.hip", "optim.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attention.hip", "norm.hip", "embed.hip", "xent.hip", "optim.hip", "fp8.hip"]
 ARCH = os.environ.get("GPTMI_ARCH", "gfx950")
 
 CFLAGS = [

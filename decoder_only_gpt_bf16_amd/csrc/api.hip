@@ -650,6 +650,41 @@ int val_bpb_reduce(int N, const float* nats, const int32_t* targets, const int32
   return GPT_OK;
 }
 
+// ------------------------------------------------------------ FP8
+size_t gpt_fp8_workspace_bytes(int64_t n) { return n > 0 ? align256((size_t)fp8_amax_parts(n) * sizeof(float)) : 0; }
+
+int gpt_fp8_quantize(int64_t n, const void* x, int fmt, void* q, float* scale, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (n <= 0) return fail(GPT_ERR_INVALID, "n must be positive");
+  if (fmt != GPT_FP8_E4M3 && fmt != GPT_FP8_E5M2) return fail(GPT_ERR_INVALID, "unknown fp8 format %d", fmt);
+  if (!x || !q || !scale) return fail(GPT_ERR_INVALID, "x, q or scale is NULL");
+  if (!aligned16(x) || !aligned16(q) || !aligned16(ws)) return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
+  const size_t need = gpt_fp8_workspace_bytes(n);
+  if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+  if (fp8_amax_parts(n) > (1L << 30)) return fail(GPT_ERR_INVALID, "n too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("fp8_quantize", launch_fp8_quantize((long)n, x, fmt, q, scale, static_cast<float*>(ws), s));
+  return GPT_OK;
+}
+
+int gpt_fp8_gemm(int M, int N, int K, const void* qa, int64_t lda, int fmt_a, const float* scale_a, const void* qb,
+                 int64_t ldb, int fmt_b, const float* scale_b, void* out, int64_t ldc, void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(GPT_ERR_INVALID, "M, N and K must be positive");
+  if ((fmt_a != GPT_FP8_E4M3 && fmt_a != GPT_FP8_E5M2) || (fmt_b != GPT_FP8_E4M3 && fmt_b != GPT_FP8_E5M2))
+    return fail(GPT_ERR_INVALID, "unknown fp8 format");
+  if (!qa || !qb || !scale_a || !scale_b || !out) return fail(GPT_ERR_INVALID, "a pointer argument is NULL");
+  if (K % 16 || lda % 16 || ldb % 16 || lda < K || ldb < K)
+    return fail(GPT_ERR_INVALID, "K, lda, ldb must be multiples of 16 with lda, ldb >= K");
+  if (N % 8 || ldc % 8 || ldc < N) return fail(GPT_ERR_INVALID, "N and ldc must be multiples of 8 with ldc >= N");
+  if (!aligned16(qa) || !aligned16(qb) || !aligned16(out)) return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
+  if ((M - 1) * lda + K >= (1L << 31) || (N - 1) * ldb + K >= (1L << 31))
+    return fail(GPT_ERR_INVALID, "operand larger than 2 GiB");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RUN("fp8_gemm", launch_fp8_gemm(M, N, K, qa, (long)lda, fmt_a, scale_a, qb, (long)ldb, fmt_b, scale_b, out,
+                                  (long)ldc, s));
+  return GPT_OK;
+}
+
 // ------------------------------------------------------------ optimizer
 static int adamw_tensors(const gpt_adamw_tensor* tensors, int count, std::vector<OptTensor>& out) {
   if (!tensors || count <= 0) return fail(GPT_ERR_INVALID, "no tensors");

@@ -208,3 +208,12 @@ size_t adamw_ws_bytes(const OptTensor* t, int count);
 hipError_t launch_adamw(const OptTensor* t, int count, float lr, float beta1, float beta2, float eps,
                         float weight_decay, int step, float max_norm, float* norm_out, void* ws,
                         hipStream_t s);
+
+// FP8 (fp8.hip).  Formats: OCP E4M3 and E5M2.
+constexpr int FP8_E4M3 = 0, FP8_E5M2 = 1;
+long fp8_amax_parts(long n);
+// scal (device float[3]) <- scale, amax, 1 / scale; q <- codes; part: fp8_amax_parts(n) floats
+hipError_t launch_fp8_quantize(long n, const void* x, int fmt, void* q, float* scal, float* part, hipStream_t s);
+// out (bf16, ldc) = A B^T * scal_a[2] * scal_b[2]; A [M][lda], B [N][ldb] codes, k contiguous
+hipError_t launch_fp8_gemm(int M, int N, int K, const void* A, long lda, int fa, const float* scal_a, const void* B,
+                           long ldb, int fb, const float* scal_b, void* out, long ldc, hipStream_t s);

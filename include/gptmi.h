@@ -225,6 +225,33 @@ int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors,
                    void* stream);
 size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count);
 
+/* ---- FP8 GEMMs ---- */
+
+#define GPT_FP8_E4M3 0   /* OCP E4M3: bias 7, largest finite 448, no infinities */
+#define GPT_FP8_E5M2 1   /* OCP E5M2: bias 15, largest finite 57344           */
+
+/* Dynamic per-tensor FP8 quantization ([nanochat] 6.2, FP8 paragraph; [d20]
+ * Pretraining row: the published run trained its matmuls in FP8).  x: bf16
+ * [n].  scale: device fp32 [3] receiving s = fmt_max / amax (1 when amax is
+ * 0), amax = max |x| and 1 / s.  q: [n] bytes receiving the code of
+ * clamp(x * s, -fmt_max, fmt_max) (product in fp32) rounded to nearest even.
+ * ws: gpt_fp8_workspace_bytes(n) bytes.  Deterministic.  Errors: INVALID,
+ * WORKSPACE, HIP. */
+int gpt_fp8_quantize(int64_t n, const void* x, int fmt, void* q, float* scale,
+                     void* ws, size_t ws_bytes, void* stream);
+size_t gpt_fp8_workspace_bytes(int64_t n);
+
+/* out[m][n] = sum_k qa[m][k] qb[n][k] * inv_a * inv_b (inv = element 2 of
+ * the quantizer's scale array), bf16 [M][ldc] output, fp32 accumulation on
+ * the 8-bit MFMA.  qa [M][lda], qb [N][ldb] are codes of formats fmt_a,
+ * fmt_b with k contiguous (a Linear forward: activations times the weight
+ * [out, in]; an input gradient with a transposed weight).  K, lda and ldb
+ * multiples of 16; N and ldc multiples of 8; pointers 16-byte aligned; each
+ * operand under 2 GiB.  Errors: INVALID, HIP. */
+int gpt_fp8_gemm(int M, int N, int K, const void* qa, int64_t lda, int fmt_a,
+                 const float* scale_a, const void* qb, int64_t ldb, int fmt_b,
+                 const float* scale_b, void* out, int64_t ldc, void* stream);
+
 /* ---- helpers used to assemble a full model step (same conventions) ---- */
 
 /* x0[n] = wte[ids[n]] (+ wpe[t] with learned positions, cfg->rope == 0).

@@ -1,0 +1,107 @@
+"""GPU parity of the FP8 path: dynamic per-tensor quantization (codes,
+scale and amax bit-exact against the oracle) and the FP8 GEMM on the 8-bit
+MFMA (against the oracle's float64 product of the same codes).
+
+GEMM tolerance, from the arithmetic: products of two 8-bit floats are exact
+in fp32; the fp32 sums carry about K 2^-24 relative error and the bf16
+output rounds each element by at most 2^-9, so ||gpu - oracle|| / ||oracle||
+stays below 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decoder_only_gpt_bf16_amd import binding as B
+from decoder_only_gpt_bf16_amd import synth
+from decoder_only_gpt_bf16_amd.model import to_f64
+from tests._parity import assert_rel, print_case
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"e4m3": B.FP8_E4M3, "e5m2": B.FP8_E5M2}
+REL_FP8_GEMM = 1e-2
+
+
+def _bf16(a):
+    return torch.tensor(synth.bf16_bits(a).view(np.int16), device="cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("n,std", [(13, 1.0), (4096 * 3 + 17, 0.02), (1280 * 5120, 0.02), (8192 * 1280, 3.0)])
+def test_quantize_bit_exact(fmt, n, std):
+    print_case("fp8 quantize", fmt, n)
+    rng = np.random.default_rng(n)
+    x = synth.round_to(rng.standard_normal(n) * std, "bf16")
+    q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, B.gpt_fp8_workspace_bytes(n)), dtype=torch.uint8, device="cuda")
+    B.gpt_fp8_quantize(_bf16(x), FMT[fmt], q, sc, ws)
+    torch.cuda.synchronize()
+    v, scale, amax = O.fp8_quantize(x, fmt)
+    assert sc[1].item() == amax
+    assert sc[0].item() == scale
+    assert sc[2].item() == np.float32(1.0) / np.float32(scale)
+    codes = O.fp8_encode(v, fmt)
+    got = q.cpu().numpy()
+    np.testing.assert_array_equal(got, codes)
+
+
+def _codes(shape, fmt, rng, spread):
+    """Random values on the format's grid and their codes."""
+    v = O.fp8_round(rng.standard_normal(shape) * spread, fmt)
+    return v, O.fp8_encode(v, fmt)
+
+
+GEMMS = [
+    (300, 264, 208, "e4m3", "e4m3"),      # ragged M, N; K not a multiple of the 128-byte k tile
+    (512, 512, 1280, "e4m3", "e4m3"),
+    (256, 1280, 5120, "e5m2", "e4m3"),    # an input-gradient shape: E5M2 gradients times E4M3 weights
+    (1000, 3840, 1280, "e4m3", "e5m2"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb", GEMMS)
+def test_fp8_gemm(M, N, K, fa, fb):
+    print_case("fp8 gemm", M, N, K, fa, fb)
+    rng = np.random.default_rng(M + N + K)
+    va, ca = _codes((M, K), fa, rng, 20.0)
+    vb, cb = _codes((N, K), fb, rng, 20.0 if fb == "e4m3" else 200.0)
+    sa, sb = np.float32(37.5), np.float32(0.125)
+    sca = torch.tensor([sa, 1.0, np.float32(1.0) / sa, 0.0], dtype=torch.float32, device="cuda")
+    scb = torch.tensor([sb, 1.0, np.float32(1.0) / sb, 0.0], dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.gpt_fp8_gemm(torch.tensor(ca, device="cuda"), FMT[fa], sca, torch.tensor(cb, device="cuda"), FMT[fb], scb, out)
+    torch.cuda.synchronize()
+    ref = O.fp8_gemm(va, float(sa), vb, float(sb))
+    rep = {}
+    assert_rel("C", to_f64(out), ref, REL_FP8_GEMM, rep)
+    print(M, N, K, fa, fb, rep)
+
+
+def test_fp8_linear_end_to_end():
+    """bf16 activations and weight quantized on the GPU, then the GEMM: the
+    result matches the oracle's FP8 product and stays near the bf16 one."""
+    M, N, K = 8192, 5120, 1280
+    print_case("fp8 linear", M, N, K)
+    rng = np.random.default_rng(5)
+    x = synth.round_to(rng.standard_normal((M, K)), "bf16")
+    w = synth.round_to(rng.normal(0, 0.02, (N, K)), "bf16")
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros(4, dtype=torch.float32, device="cuda")
+    sb = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.gpt_fp8_workspace_bytes(M * K), dtype=torch.uint8, device="cuda")
+    B.gpt_fp8_quantize(_bf16(x), B.FP8_E4M3, qa, sa, ws)
+    B.gpt_fp8_quantize(_bf16(w), B.FP8_E4M3, qb, sb, ws)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    B.gpt_fp8_gemm(qa, B.FP8_E4M3, sa, qb, B.FP8_E4M3, sb, out)
+    torch.cuda.synchronize()
+    va, s_a, _ = O.fp8_quantize(x, "e4m3")
+    vb, s_b, _ = O.fp8_quantize(w, "e4m3")
+    rows = np.random.default_rng(6).choice(M, 256, replace=False)
+    got = to_f64(out)[rows]
+    ref = O.fp8_gemm(va[rows], s_a, vb, s_b)
+    assert_rel("C(sampled rows)", got, ref, REL_FP8_GEMM)
+    full = x[rows] @ w.T
+    assert np.linalg.norm(got - full) / np.linalg.norm(full) < 0.1
