@@ -158,6 +158,8 @@ def main():
                     help="also time the AdamW step over the d20 model's parameter set (HBM-bound)")
     ap.add_argument("--window", type=int, default=0,
                     help="also time the d20 block with sliding-window attention of this many keys")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time FP8 quantization and FP8 GEMMs at the d20 Linear shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
@@ -232,12 +234,14 @@ def main():
         "roofline": roof,
         "kernels": sites,
     }
-    if args.extra or args.adamw or args.window:
+    if args.extra or args.adamw or args.window or args.fp8:
         out["extra"] = extra_workloads(args) if args.extra else {}
         if args.adamw:
             out["extra"]["adamw_d20_model"] = adamw_workload(args)
         if args.window:
             out["extra"][f"d20_block_window{args.window}"] = window_workload(args, args.window)
+        if args.fp8:
+            out["extra"]["fp8_d20_linears"] = fp8_workload(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
@@ -273,6 +277,40 @@ def window_workload(args, window):
     return {"window": window, "ms": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
             "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16,
             "attn_us": {k: round(v[1] / v[0], 2) for k, v in trace.items() if k.startswith("attn")}}
+
+
+PEAK_FP8 = 5.0e15        # MI355X dense fp8 MFMA
+
+
+def fp8_workload(args):
+    """FP8 GEMMs at the d20 block's Linear shapes (tokens 8192, C 1280), codes
+    from quantizing bf16 activations and weights on the GPU; and the quantizer's
+    HBM rate (2 bytes read twice and 1 byte written per element)."""
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    Nt, C = 8192, 1280
+    shapes = {"qkv": (Nt, 3 * C, C), "fc": (Nt, 4 * C, C), "proj": (Nt, C, 4 * C), "out": (Nt, C, C)}
+    res = {}
+    ws = torch.empty(B.gpt_fp8_workspace_bytes(Nt * 4 * C), dtype=torch.uint8, device="cuda")
+    for name, (M, N, K) in shapes.items():
+        x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+        w = (0.02 * torch.randn((N, K), generator=gen, device="cuda")).to(torch.bfloat16)
+        qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+        sa = torch.zeros(4, device="cuda")
+        sb = torch.zeros(4, device="cuda")
+        B.gpt_fp8_quantize(w, B.FP8_E4M3, qb, sb, ws)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        qms = time_steps(lambda: B.gpt_fp8_quantize(x, B.FP8_E4M3, qa, sa, ws), args.steps, args.warmup)
+        gms = time_steps(lambda: B.gpt_fp8_gemm(qa, B.FP8_E4M3, sa, qb, B.FP8_E4M3, sb, out), args.steps, args.warmup)
+        flop = 2.0 * M * N * K
+        res[name] = {"M": M, "N": N, "K": K, "gemm_us": gms * 1e3, "tflops": flop / (gms * 1e-3) / 1e12,
+                     "fp8_peak_frac": flop / (gms * 1e-3) / PEAK_FP8, "quant_us": qms * 1e3,
+                     "quant_GBps": 5.0 * M * K / (qms * 1e-3) / 1e9}
+        del x, w, qa, qb, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def adamw_workload(args):
