@@ -55,8 +55,18 @@ __global__ __launch_bounds__(Q_THREADS) void amax_k(long n, const bf16* __restri
 // scal[0] = scale, scal[1] = amax, scal[2] = 1 / scale
 __global__ __launch_bounds__(Q_THREADS) void amax_finish_k(int nparts, const float* __restrict__ part, int fmt,
                                                            float* __restrict__ scal) {
+  // one block walks all partials: their loads go out 16 at a time
+  constexpr int U = 16;
   float m = 0.0f;
-  for (int i = threadIdx.x; i < nparts; i += Q_THREADS) m = fmaxf(m, part[i]);
+  int i = threadIdx.x;
+  for (; i + (U - 1) * Q_THREADS < nparts; i += U * Q_THREADS) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[i + u * Q_THREADS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, v[u]);
+  }
+  for (; i < nparts; i += Q_THREADS) m = fmaxf(m, part[i]);
   m = wave_max(m);
   __shared__ float red[Q_THREADS / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;

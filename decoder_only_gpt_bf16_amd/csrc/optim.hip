@@ -77,11 +77,22 @@ __global__ __launch_bounds__(OPT_THREADS) void sumsq_k(OptTable T, double* __res
   if (threadIdx.x == 0) part[blockIdx.x] = t;
 }
 
-// scal[0] = clip factor, scal[1] = global norm (before clipping)
+// scal[0] = clip factor, scal[1] = global norm (before clipping).  Thread t
+// adds partials t, t + 256, ... in index order; their loads are issued 32 at
+// a time, since one block alone walks the whole partial array
 __global__ __launch_bounds__(OPT_THREADS) void norm_k(const double* __restrict__ part, int nparts, float max_norm,
                                                       float* __restrict__ scal, float* __restrict__ norm_out) {
+  constexpr int U = 32;
   double s = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += OPT_THREADS) s += part[i];
+  int i = threadIdx.x;
+  for (; i + (U - 1) * OPT_THREADS < nparts; i += U * OPT_THREADS) {
+    double v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[i + u * OPT_THREADS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  for (; i < nparts; i += OPT_THREADS) s += part[i];
   const double total = block_sum_d(s);
   if (threadIdx.x == 0) {
     const double norm = sqrt(total);
