@@ -164,16 +164,41 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
   }
 }
 
-__global__ void colsum_finish_k(int C, int nblk, const float* __restrict__ part, float* __restrict__ out,
-                                int accumulate) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
+// out[c] (+)= sum of part[b][c] over b < nblk.  A block takes CF_COLS
+// columns; CF_SEGS threads per column each add a contiguous run of the
+// partials in order, their loads issued CF_U at a time, and the runs' sums
+// are then added in run order: a fixed order for any launch.
+constexpr int CF_COLS = 16, CF_SEGS = 16, CF_U = 16;
+__global__ __launch_bounds__(CF_COLS * CF_SEGS) void colsum_finish_k(int C, int nblk, const float* __restrict__ part,
+                                                                     float* __restrict__ out, int accumulate) {
+  const int lc = threadIdx.x % CF_COLS, seg = threadIdx.x / CF_COLS;
+  const int c = blockIdx.x * CF_COLS + lc;
+  const int per = (nblk + CF_SEGS - 1) / CF_SEGS;
+  const int b1 = min(nblk, (seg + 1) * per);
   float s = 0.0f;
-  for (int b = 0; b < nblk; ++b) s += part[(long)b * C + c];
-  out[c] = accumulate ? out[c] + s : s;
+  if (c < C) {
+    int b = seg * per;
+    for (; b + CF_U <= b1; b += CF_U) {
+      float v[CF_U];
+#pragma unroll
+      for (int u = 0; u < CF_U; ++u) v[u] = part[(long)(b + u) * C + c];
+#pragma unroll
+      for (int u = 0; u < CF_U; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += part[(long)b * C + c];
+  }
+  __shared__ float red[CF_SEGS][CF_COLS];
+  red[seg][lc] = s;
+  __syncthreads();
+  if (seg == 0 && c < C) {
+    float t = red[0][lc];
+    for (int q = 1; q < CF_SEGS; ++q) t += red[q][lc];
+    out[c] = accumulate ? out[c] + t : t;
+  }
 }
 
-// Column sums of x [N, C] (ld) into per-block partials [nblk][C].
+// Column sums of x [N, C] (ld) into per-block partials [nblk][C]; a thread
+// adds its column over the block's rows in order, loads issued 16 at a time.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_part_k(int N, int C, long ld, const T* __restrict__ x,
                                                      float* __restrict__ part, int rows_per_blk) {
@@ -181,12 +206,21 @@ __global__ __launch_bounds__(256) void colsum_part_k(int N, int C, long ld, cons
   if (c >= C) return;
   const int r0 = blockIdx.y * rows_per_blk;
   const int r1 = min(N, r0 + rows_per_blk);
+  constexpr int U = 16;
   float s = 0.0f;
-  for (int r = r0; r < r1; ++r) s += to_f32(x[(long)r * ld + c]);
+  int r = r0;
+  for (; r + U <= r1; r += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = to_f32(x[(long)(r + u) * ld + c]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  for (; r < r1; ++r) s += to_f32(x[(long)r * ld + c]);
   part[(long)blockIdx.y * C + c] = s;
 }
 
-constexpr int COLSUM_ROWS = 128;
+constexpr int COLSUM_ROWS = 64;
 
 }  // namespace
 
@@ -225,7 +259,8 @@ hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, con
 
 hipError_t launch_colsum_finish(int C, int nblk, const float* part, float* out, int accumulate,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(colsum_finish_k, dim3(cdiv(C, 256)), dim3(256), 0, s, C, nblk, part, out, accumulate);
+  hipLaunchKernelGGL(colsum_finish_k, dim3(cdiv(C, CF_COLS)), dim3(CF_COLS * CF_SEGS), 0, s, C, nblk, part, out,
+                     accumulate);
   return hipGetLastError();
 }
 
