@@ -264,7 +264,7 @@ XentWs xent_layout(const Dims& d, int N, Arena& a) {
   int P = 0;
   for (int c = 0; c < x.nchunk; ++c) {
     const int w = std::min(x.Vc, V - c * x.Vc);
-    P += 2 * cdiv(w, 256);
+    P += (256 / xent_part_cols()) * cdiv(w, 256);
   }
   x.P = P;
   const bool mfma = d.dtype == 1;
@@ -439,7 +439,8 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   RUN("out_gemm", launch_gemm(g, ty, nullptr, s));
   RUN("norm2_fwd", launch_norm_fwd(ty, kind, d.N, C, sv.x1, w->ln2_w, opt(cfg, w->ln2_b), cfg->norm_eps, sv.a2, sv.stats2, s));
   g = lin_fwd(d, sv.a2, C, w->w_fc, 4 * C, EPI_GELU);
-  g.out = sv.u; g.out2 = sv.g; g.ldc = 4 * C; g.bias = opt(cfg, w->b_fc);
+  // inference keeps no GELU'(u): the epilogue then writes GELU(u) only
+  g.out = saved ? sv.u : nullptr; g.out2 = sv.g; g.ldc = 4 * C; g.bias = opt(cfg, w->b_fc);
   RUN("fc_gemm_gelu", launch_gemm(g, ty, nullptr, s));
   g = lin_fwd(d, sv.g, 4 * C, w->w_proj, C, EPI_STORE);
   g.out = y; g.ldc = C; g.bias = opt(cfg, w->b_proj); g.resid = sv.x1; g.ldr = C;
@@ -577,7 +578,7 @@ static int xent_impl(const gpt_config* cfg, int N, const void* h, const void* W,
       g.epi = EPI_XENT_STATS;
       g.tgt = targets; g.col_offset = v0; g.part = x.part; g.part_ld = x.P;
       int off = 0;
-      for (int q = 0; q < c; ++q) off += 2 * cdiv(std::min(x.Vc, V - q * x.Vc), 256);
+      for (int q = 0; q < c; ++q) off += (256 / xent_part_cols()) * cdiv(std::min(x.Vc, V - q * x.Vc), 256);
       g.part_off = off; g.ztgt = x.ztgt;
       RUN("xent_stats_gemm", launch_gemm(g, ty, nullptr, s));
     } else {

@@ -113,6 +113,7 @@ __device__ __forceinline__ void epiW(const GemmParams& p, int m, int n, float* v
     T* o2 = reinterpret_cast<T*>(p.out2) + (long)m * p.ldc + n;
     if (full) storeW<T, W>(o2, g);
     else for (int e = 0; e < W; ++e) if (n + e < p.N) o2[e] = from_f32<T>(g[e]);
+    if (!p.out) return;  // forward only: nothing keeps GELU'(u)
   } else if constexpr (EPI == EPI_GELU_BWD) {
     const T* dg = reinterpret_cast<const T*>(p.aux) + (long)m * p.ldaux + n;
     if (full && use_pre) take_pre(t);
@@ -862,13 +863,13 @@ Plan plan_mfma(const GemmDesc& d) {
 }
 
 // 256 x 256 tiles run 8 waves (two per SIMD, 128 x 64 each, or 64 x 128 for
-// the fused RoPE / QK-norm epilogue, whose waves each hold one head); the LM-head
-// statistics keep 4 waves so that a wave covers the 128 columns of one
-// (max, sum exp) partial.  128 x 128 tiles run 4 waves of 64 x 64.
+// the fused RoPE / QK-norm epilogue, whose waves each hold one head); in the
+// LM-head statistics a wave's 64 columns make one (max, sum exp) partial.
+// 128 x 128 tiles run 4 waves of 64 x 64.
 template <bool AK, bool BKm, int EPI, int BMv, int BNv>
 hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  if constexpr (BMv == 256 && EPI != EPI_XENT_STATS)
+  if constexpr (BMv == 256)
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2>), grid, dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2>), grid, dim3(256), 0, s, p);
@@ -969,7 +970,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_k(TransposeJobs J) {
 
 }  // namespace
 
-int xent_part_cols() { return 128; }
+int xent_part_cols() { return 64; }
 
 size_t gemm_split_scratch_bytes(const GemmDesc& d, int dtype) {
   if (dtype != 1 || d.epi != EPI_F32) return 0;

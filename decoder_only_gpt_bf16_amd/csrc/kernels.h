@@ -15,7 +15,7 @@
 // ---------------------------------------------------------------------------
 enum EpiKind {
   EPI_STORE = 0,      // out(T) = acc (+ bias[n]) (+ resid[m, n])
-  EPI_GELU = 1,       // u = acc + bias[n]; out(T) = gelu'(u); out2(T) = gelu(u)
+  EPI_GELU = 1,       // u = acc + bias[n]; out(T) = gelu'(u) (skipped when out is NULL); out2(T) = gelu(u)
   EPI_GELU_BWD = 2,   // out(T) = acc * aux[m, n] (aux = the stored gelu'(u))
   EPI_F32 = 3,        // out(f32) = acc (+ out if accumulate)
   EPI_XENT_STATS = 4, // per (row, 128-col block): max and sum exp; target logit

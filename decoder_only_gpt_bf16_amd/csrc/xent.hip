@@ -3,7 +3,7 @@
 // Cross-entropy ("nanoGPT — Karpathy's minimal GPT pretraining repo",
 // train.py: mean over tokens of the negative log-probability of the next
 // token): per token, nats = logsumexp(z) - z[target].  The bf16 path gets
-// (max, sum exp) partials per 128-column block from the LM-head GEMM
+// (max, sum exp) partials per 64-column block from the LM-head GEMM
 // epilogue; xent_finish_k merges them per row.  The fp32 path materialises
 // one vocabulary chunk of logits at a time and keeps running statistics.
 //
