@@ -13,6 +13,7 @@ the timed region starts.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -372,6 +373,19 @@ def extra_workloads(args):
     res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
                    "loss": m.loss.item()}
     del m
+    torch.cuda.empty_cache()
+    # the whole d20 training step at the block's shape: 20 blocks, untied head
+    # (V 32768), B 4, T 2048, fwd + bwd with the vocabulary-chunked loss
+    w = dataclasses.replace(synth.D20_EVAL, name="d20_train_step", B=4, kind="step")
+    ids, y, P, tb = synth.make_model_inputs(w)
+    m = ModelRunner(w.cfg, w.B, w.T, P, tb)
+    m.set_batch(ids, y)
+    ms = time_steps(m.train_step, max(3, args.steps // 4), 2)
+    C, L, V, N = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T
+    f = L * block_flops(w.B, w.T, C, w.cfg.n_head) + 6.0 * N * C * V
+    res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
+                   "loss": m.loss.item()}
+    del m, P
     torch.cuda.empty_cache()
     w = synth.D20_EVAL
     ids, y, P, tb = synth.make_model_inputs(w)
