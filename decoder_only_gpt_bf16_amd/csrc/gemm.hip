@@ -876,8 +876,10 @@ hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256 x 160 tiles (N a multiple of 160, e.g. 1280 = 8 x 160 with M = 8192:
-// exactly one tile per CU) run 4 waves of 64 x 160.
+// Wide tiles: 256 x 320 (8 waves of 64 x 160) where they fill the CUs in
+// whole rounds and 256 x 256 would not; 256 x 160 (N a multiple of 160, e.g.
+// 1280 = 8 x 160 with M = 8192: exactly one tile per CU) as 8 waves of
+// 32 x 160, two per SIMD.
 template <bool AK, bool BKm, int EPI>
 hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
   if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
