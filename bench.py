@@ -30,10 +30,10 @@ CSRC = os.path.join(HERE, "decoder_only_gpt_bf16_amd", "csrc")
 # call site -> (kernels as named in the counter summary, their source files);
 # sites that share a GEMM instance with others have no entry
 SITE_KERNEL = {
-    "attn_fwd": (["attn_fwd_mfma<128>"], "attention"),
+    "attn_fwd": (["attn_fwd_mfma<128, true>"], "attention"),
     "attn_bwd_dkdv": (["attn_bwd_dkdv_mfma<128>"], "attention"),
     "attn_bwd_dq": (["attn_bwd_dq_mfma<128>"], "attention"),
-    "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 4>"], "gemm"),
+    "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 2>"], "gemm"),
     "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4>"], "gemm"),
     "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4>"], "gemm"),
     "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2>", "streamk_fixup<256, 256>"], "gemm"),
