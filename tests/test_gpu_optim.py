@@ -105,6 +105,16 @@ def test_adamw_block_parameter_set(name):
     _compare(host, dev, ref, norms, ref_norms)
 
 
+def test_adamw_norm_many_partials():
+    # 70 M elements: 8545 partials of the squared norm, enough for the norm
+    # kernel's batched loads (32 x 256 of them at a time) to run
+    shapes = [(70_000_000,)]
+    print_case("adamw 70M")
+    host, dev, norms = _run(shapes, [1], [False], 1.0, steps=1, seed=3)
+    ref, ref_norms = _oracle(host, [1], 1.0, steps=1)
+    _compare(host, dev, ref, norms, ref_norms)
+
+
 def test_adamw_reproducible():
     shapes, decay, want16 = MIXED
     print_case("adamw twice")
