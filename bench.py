@@ -134,27 +134,39 @@ def cpu_baseline(w, min_s=12.0):
             "sample": f"{n} sequences (B=1, T={w.T} each) of the d20 block fwd+bwd in float64 NumPy, {dt:.1f} s"}
 
 
-def time_steps(fn, steps, warmup):
+def time_steps(fn, steps, warmup, per_step=None):
+    """Mean ms per step of `steps` calls bracketed by synchronizations
+    (hipEvents on the current stream, the library's stream).  per_step (a
+    list) receives each step's own event-timed ms as well."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if per_step is not None else None
     a.record()
-    for _ in range(steps):
+    for i in range(steps):
+        if ev:
+            ev[i].record()
         fn()
+    if ev:
+        ev[steps].record()
     b.record()
     torch.cuda.synchronize()
+    if ev:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return a.elapsed_time(b) / steps
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", action="store_true", help="also time the GPT-2 block, GPT-2 step and d20 eval")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the headline workload (no other configs, LM head or clock sample)")
+    ap.add_argument("--extra", action="store_true", help="also time the whole d20 training step (20 blocks + head)")
     ap.add_argument("--adamw", action="store_true",
                     help="also time the AdamW step over the d20 model's parameter set (HBM-bound)")
     ap.add_argument("--window", type=int, default=0,
@@ -188,7 +200,9 @@ def main():
     x, dy, p = synth.make_block_inputs(w)
     r = BlockRunner(cfg, w.B, w.T, x, dy, p)
     torch.cuda.synchronize()
-    ms = time_steps(r.step, args.steps, args.warmup)
+    per = []
+    ms = time_steps(r.step, args.steps, args.warmup, per)
+    per.sort()
     flops = block_flops(w.B, w.T, cfg.n_embd, cfg.n_head)
     tok_s = w.B * w.T / (ms * 1e-3)
 
@@ -231,10 +245,17 @@ def main():
         "config": {"workload": "d20 block fwd+bwd (RMSNorm, RoPE, QK-norm, GELU MLP)", "batch": w.B, "seq_len": w.T,
                    "n_embd": cfg.n_embd, "n_head": cfg.n_head, "head_dim": cfg.head_dim},
         "mfma_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4),
+        "step_ms_median": round(per[len(per) // 2], 4), "step_ms_min": round(per[0], 4),
         "flop_per_step": flops,
         "roofline": roof,
         "kernels": sites,
     }
+    if not args.quick:
+        out["gpu_clock_mhz"] = clock_during(r.step)
+        del r
+        torch.cuda.empty_cache()
+        out["configs"] = config_workloads(args)
+        out["lm_head"] = lm_head_workloads(args)
     if args.extra or args.adamw or args.window or args.fp8:
         out["extra"] = extra_workloads(args) if args.extra else {}
         if args.adamw:
@@ -351,7 +372,13 @@ def adamw_workload(args):
     return res
 
 
-def extra_workloads(args):
+def config_workloads(args):
+    """The other configurations at their full sizes: the GPT-2 124M block
+    fwd+bwd (B 8, T 1024), the 12-layer GPT-2 124M training step (B 16,
+    T 1024, tied head V 50304) and the 20-layer d20 val-bpb evaluation (B 8,
+    T 2048, untied head V 32768, forward only).  Useful FLOPs: 6 per
+    parameter-FLOP of the Linear layers and the head, causal attention on the
+    lower triangle."""
     import torch
     from decoder_only_gpt_bf16_amd import synth
     from decoder_only_gpt_bf16_amd.model import BlockRunner, ModelRunner
@@ -359,23 +386,180 @@ def extra_workloads(args):
     w = synth.GPT2_BLOCK
     x, dy, p = synth.make_block_inputs(w)
     r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
-    ms = time_steps(r.step, args.steps, args.warmup)
+    per = []
+    ms = time_steps(r.step, args.steps, args.warmup, per)
     f = block_flops(w.B, w.T, w.cfg.n_embd, w.cfg.n_head)
-    res[w.name] = {"tokens_per_s": w.B * w.T / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16}
+    res[w.name] = {"tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1), "ms": round(ms, 4),
+                   "ms_median": round(sorted(per)[len(per) // 2], 4), "mfma_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4),
+                   "flop_per_step": f}
     del r
     w = synth.GPT2_STEP
     ids, y, P, tb = synth.make_model_inputs(w)
     m = ModelRunner(w.cfg, w.B, w.T, P, tb)
     m.set_batch(ids, y)
-    ms = time_steps(m.train_step, max(3, args.steps // 4), 2)
+    per = []
+    ms = time_steps(m.train_step, 5, 2, per)
     C, L, V, N = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T
     f = L * block_flops(w.B, w.T, C, w.cfg.n_head) + 6.0 * N * C * V
-    res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
-                   "loss": m.loss.item()}
-    del m
+    res[w.name] = {"tokens_per_s": round(N / (ms * 1e-3), 1), "ms": round(ms, 3),
+                   "ms_median": round(sorted(per)[len(per) // 2], 3), "mfma_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4),
+                   "flop_per_step": f, "loss": m.loss.item()}
+    del m, P
     torch.cuda.empty_cache()
-    # the whole d20 training step at the block's shape: 20 blocks, untied head
-    # (V 32768), B 4, T 2048, fwd + bwd with the vocabulary-chunked loss
+    w = synth.D20_EVAL
+    ids, y, P, tb = synth.make_model_inputs(w)
+    m = ModelRunner(w.cfg, w.B, w.T, P, tb, train=False)
+    m.set_batch(ids, y)
+    per = []
+    ms = time_steps(m.eval_step, 5, 2, per)
+    C, L, V, N, T = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T, w.T
+    f = L * (2 * 12 * C * C * N + 2 * w.B * w.cfg.n_head * (C // w.cfg.n_head) * T * T) + 2.0 * N * C * V
+    m.sum_nats.zero_()
+    m.sum_bytes.zero_()
+    m.eval_step()
+    res[w.name] = {"tokens_per_s": round(N / (ms * 1e-3), 1), "ms": round(ms, 3),
+                   "ms_median": round(sorted(per)[len(per) // 2], 3), "mfma_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4),
+                   "flop_per_step": f, "bpb": m.sum_nats.item() / (math.log(2) * m.sum_bytes.item())}
+    del m, P
+    torch.cuda.empty_cache()
+    return res
+
+
+# LM-head call sites: algorithmic work per launch (N tokens, C width, Vc
+# columns of the launch's vocabulary chunk)
+def head_site_work(name, N, C, Vc, P):
+    if name in ("xent_stats_gemm", "xent_grad_gemm", "xent_dh_gemm", "xent_dw_gemm"):
+        return "mfma", 2.0 * N * C * Vc
+    if name == "xent_finish":
+        # per row: P (max, sum exp) partials read, target logit read; lse, nats written
+        return "hbm", N * (8.0 * P + 12.0)
+    if name == "xent_dh_convert":
+        return "hbm", N * C * (4.0 + 2.0)
+    return None, None
+
+
+def lm_head_workloads(args):
+    """The vocabulary-chunked LM head with softmax cross-entropy at the two
+    full-size heads: the GPT-2 124M step (N 16384, C 768, tied V 50304:
+    forward + backward: statistics, logit gradient, dh and dW per chunk of
+    8192 columns) and the d20 evaluation (N 16384, C 1280, V 32768: forward
+    only).  The softmax statistics ride in the logit GEMM's epilogue, so no
+    logit chunk is written to HBM; each call site is timed with hipEvents on
+    the library's stream and priced against MFMA (its GEMM FLOPs) or HBM
+    (the bytes it must move)."""
+    import numpy as np
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import upload_i32, workspace
+    res = {}
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for name, w, grad in (("gpt2_124m_step_head", synth.GPT2_STEP, True), ("d20_val_bpb_head", synth.D20_EVAL, False)):
+        cfg, N = w.cfg, w.B * w.T
+        C, V = cfg.n_embd, cfg.vocab_size
+        c = B.make_config(cfg)
+        ws = workspace(c, w.B, w.T)
+        h = torch.randn((N, C), generator=gen, device="cuda").to(torch.bfloat16)
+        W = (0.02 * torch.randn((V, C), generator=gen, device="cuda")).to(torch.bfloat16)
+        tgt = upload_i32(np.random.default_rng(5).integers(0, V, N))
+        loss = torch.zeros(1, device="cuda")
+        nats = torch.zeros(N, device="cuda")
+        dh = torch.empty((N, C), dtype=torch.bfloat16, device="cuda") if grad else None
+        dW = torch.empty((V, C), dtype=torch.float32, device="cuda") if grad else None
+        call = lambda: B.lm_head_xent_fwd_bwd(c, N, h, W, tgt, 1.0 / N, loss, nats, dh, dW, 0, ws)  # noqa: E731
+        steps = max(5, args.steps // 5)
+        ms = time_steps(call, steps, 2)
+        B.gpt_trace_begin(64 * steps)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        trace = B.gpt_trace_end()
+        Vc = min(V, 8192)
+        nchunk = -(-V // Vc)
+        P = sum(4 * -(-min(Vc, V - i * Vc) // 256) for i in range(nchunk))
+        sites = {}
+        for site, (n, us) in trace.items():
+            avg = us / n
+            e = {"launches_per_call": n / steps, "avg_us": round(avg, 2)}
+            bound, work = head_site_work(site, N, C, Vc, P)
+            if bound:
+                e["bound"] = bound
+                e["frac"] = round(work / (avg * 1e-6) / (PEAK_BF16 if bound == "mfma" else PEAK_HBM), 4)
+                tr = measured_traffic(site)
+                if tr is not None:
+                    e["traffic"] = tr
+            sites[site] = e
+        flops = (6.0 if grad else 2.0) * N * C * V
+        res[name] = {"N": N, "C": C, "V": V, "fwd_bwd": grad, "ms": round(ms, 4),
+                     "mfma_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4),
+                     # bytes a separate softmax-xent pass over bf16 logit chunks would
+                     # read (and write, for the gradient); none of it exists here
+                     "unfused_chunk_bytes": (3 if grad else 1) * 2.0 * N * V,
+                     "sites": sites}
+        del h, W, dh, dW, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def clock_during(fn, seconds=1.5):
+    """Shader clock (MHz) sampled from amd-smi while fn runs back to back on
+    the GPU; None when amd-smi is not usable."""
+    import subprocess
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                                     timeout=5).stdout
+                samples.append(_gfx_clock(json.loads(out)))
+            except Exception:
+                samples.append(None)
+                return
+
+    t = threading.Thread(target=sample, daemon=True)
+    t0 = time.time()
+    t.start()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join(timeout=10)
+    vals = [v for v in samples if v]
+    return {"mhz": vals, "source": "amd-smi metric -c, sampled during back-to-back steps"} if vals else None
+
+
+def _gfx_clock(js):
+    """Mean current GFX clock (MHz) over the first GPU's XCDs (amd-smi's
+    gfx_0 .. gfx_7 entries), or None."""
+    vals = []
+
+    def walk(o):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                if k.lower().startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                    try:
+                        vals.append(float(v["clk"]["value"]))
+                    except (KeyError, TypeError, ValueError):
+                        pass
+                else:
+                    walk(v)
+        elif isinstance(o, list) and o:
+            walk(o[0])
+    walk(js)
+    return sum(vals) / len(vals) if vals else None
+
+
+def extra_workloads(args):
+    """The whole d20 training step at the block's shape: 20 blocks, untied
+    head (V 32768), B 4, T 2048, fwd + bwd with the vocabulary-chunked loss."""
+    import torch
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import ModelRunner
+    res = {}
     w = dataclasses.replace(synth.D20_EVAL, name="d20_train_step", B=4, kind="step")
     ids, y, P, tb = synth.make_model_inputs(w)
     m = ModelRunner(w.cfg, w.B, w.T, P, tb)
@@ -387,15 +571,6 @@ def extra_workloads(args):
                    "loss": m.loss.item()}
     del m, P
     torch.cuda.empty_cache()
-    w = synth.D20_EVAL
-    ids, y, P, tb = synth.make_model_inputs(w)
-    m = ModelRunner(w.cfg, w.B, w.T, P, tb, train=False)
-    m.set_batch(ids, y)
-    ms = time_steps(m.eval_step, max(3, args.steps // 4), 2)
-    C, L, V, N, T = w.cfg.n_embd, w.cfg.n_layer, w.cfg.vocab_size, w.B * w.T, w.T
-    f = L * (2 * 12 * C * C * N + 2 * w.B * w.cfg.n_head * (C // w.cfg.n_head) * T * T) + 2.0 * N * C * V
-    res[w.name] = {"tokens_per_s": N / (ms * 1e-3), "ms": ms, "mfma_frac": f / (ms * 1e-3) / PEAK_BF16,
-                   "bpb": m.sum_nats.item() / (math.log(2) * m.sum_bytes.item())}
     return res
 
 

@@ -92,6 +92,8 @@ struct Dims {
   size_t es;  // storage element size
 };
 
+constexpr long MAX_OPERAND_BYTES = 1L << 31;
+
 int check_cfg(const gpt_config* cfg, Dims& d) {
   if (!cfg) return fail(GPT_ERR_INVALID, "cfg is NULL");
   if (cfg->n_head <= 0 || cfg->n_embd <= 0 || cfg->block_size <= 0 || cfg->vocab_size <= 0)
@@ -121,7 +123,11 @@ int check_bt(const gpt_config* cfg, int B, int T, Dims& d) {
   if (st) return st;
   if (B <= 0 || T <= 0) return fail(GPT_ERR_INVALID, "B and T must be positive (B=%d T=%d)", B, T);
   if (T > cfg->block_size) return fail(GPT_ERR_INVALID, "T=%d exceeds block_size=%d", T, cfg->block_size);
-  if ((long)B * T * 4L * cfg->n_embd >= (1L << 31) * 8L) return fail(GPT_ERR_UNSUPPORTED, "batch too large");
+  // the kernels address their operands through buffer descriptors with
+  // 31-bit byte offsets: the largest one, [B*T, 4C] (GELU(u), GELU'(u), du),
+  // must stay below 2 GiB, so larger batches are refused before any launch
+  if ((long)B * T * 4L * cfg->n_embd * (long)d.es >= MAX_OPERAND_BYTES)
+    return fail(GPT_ERR_UNSUPPORTED, "B*T*4*n_embd = %ld elements: an operand of 2 GiB or more", (long)B * T * 4L * cfg->n_embd);
   d.B = B;
   d.T = T;
   d.N = B * T;
@@ -558,6 +564,13 @@ static int xent_impl(const gpt_config* cfg, int N, const void* h, const void* W,
   if (!aligned16(h) || !aligned16(W) || !aligned16(dh) || !aligned16(dW) || !aligned16(ws))
     return fail(GPT_ERR_INVALID, "buffer not 16-byte aligned");
   d.B = 1; d.T = N; d.N = N;
+  {
+    // the logit-gradient chunk [N, min(V, chunk)] and h [N, C] are GEMM
+    // operands read through 31-bit buffer offsets
+    const long ldz = (std::min(d.V, XENT_CHUNK) + 7) / 8 * 8;
+    if ((long)N * std::max<long>(ldz, d.C) * (long)d.es >= MAX_OPERAND_BYTES)
+      return fail(GPT_ERR_UNSUPPORTED, "N = %d: a logit chunk or h operand of 2 GiB or more", N);
+  }
   const size_t need = xent_ws_bytes(d, N);
   if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -756,6 +756,9 @@ __global__ __launch_bounds__(256) void streamk_fixup(GemmGroup g, StreamKPlan k)
   if (m >= p.M || n >= p.N) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j <= last - first; ++j) {
+    // a block with an empty unit range (rem * nk < G) wrote no slot; every
+    // other block in first..last holds a piece of this tile
+    if (sk_units_begin(k, first + j) == sk_units_begin(k, first + j + 1)) continue;
     const float4 v = *reinterpret_cast<const float4*>(k.part + ((long)rt * k.S + j) * (BM * BN) + e);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }

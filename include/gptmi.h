@@ -122,8 +122,12 @@ size_t gpt_workspace_bytes(const gpt_config* cfg, int B, int T);
  *         RoPE table it reads too); NULL runs inference only (intermediates
  *         then live in the workspace, which is otherwise not touched).
  * Errors: INVALID (null pointer, B/T <= 0, T > block_size, n_embd % n_head,
- * odd head_dim with rope), UNSUPPORTED (bf16 with head_dim not in {64,128}
- * or C % 8 != 0), WORKSPACE, HIP. */
+ * odd head_dim with rope), UNSUPPORTED (head_dim not a multiple of 8 or
+ * above 128, n_embd above 2048, or B*T*4*n_embd elements of 2 GiB or more:
+ * the largest operand, refused before any launch), WORKSPACE, HIP.  In bf16,
+ * head_dim 64 and 128 run the matrix-core attention kernels; other head
+ * dims run a slower vector-ALU attention path (same function, its own
+ * rounding). */
 int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x,
                   const gpt_block_weights* w, void* y, void* saved,
                   void* ws, size_t ws_bytes, void* stream);
@@ -149,7 +153,8 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x,
  *   dh       [N, C] gradient wrt h (dtype), or NULL for forward only
  *   dW       [V, C] fp32 gradient wrt W (accumulate 0/1), or NULL
  * The logits are produced one vocabulary chunk at a time and the full
- * [N, V] matrix never exists in memory.  Errors: INVALID, WORKSPACE, HIP. */
+ * [N, V] matrix never exists in memory.  Errors: INVALID, UNSUPPORTED
+ * (N * max(min(V, 8192), C) elements of 2 GiB or more), WORKSPACE, HIP. */
 int lm_head_xent_fwd_bwd(const gpt_config* cfg, int N, const void* h,
                          const void* W, const int32_t* targets,
                          float loss_scale, float* loss, float* nats,
@@ -254,27 +259,40 @@ int gpt_fp8_gemm(int M, int N, int K, const void* qa, int64_t lda, int fmt_a,
 
 /* ---- helpers used to assemble a full model step (same conventions) ---- */
 
-/* x0[n] = wte[ids[n]] (+ wpe[t] with learned positions, cfg->rope == 0).
- * ids int32 [B*T]; wte [V, C]; wpe [block_size, C] or NULL when rope. */
+/* Token embedding ([nanoGPT] model.py section: the token embedding wte,
+ * plus the learned absolute position embedding wpe in the nanoGPT form; the
+ * nanochat form uses RoPE in the attention instead, [d20] Architecture row):
+ * x0[n] = wte[ids[n]] (+ wpe[t] with learned positions, cfg->rope == 0).
+ * ids int32 [B*T] (an id outside [0, V) gives a zero token row); wte [V, C];
+ * wpe [block_size, C] or NULL when rope; x0 [B*T, C] (dtype).  Errors:
+ * INVALID, UNSUPPORTED (as gpt_block_fwd), HIP. */
 int gpt_embed_fwd(const gpt_config* cfg, int B, int T, const int32_t* ids,
                   const void* wte, const void* wpe, void* x0, void* stream);
 
-/* dwte[v] (+)= sum of dx0 rows with id v (fixed summation order: by
+/* Backward of gpt_embed_fwd ([nanoGPT] model.py section; with weight tying
+ * the head's gradient is added into the same dwte, accumulate = 1):
+ * dwte[v] (+)= sum of dx0 rows with id v (fixed summation order: by
  * position), dwpe[t] (+)= sum over the batch of dx0[b, t]; fp32 outputs.
  * dwpe may be NULL.  Rows of dwte that no id touches are zeroed when
- * accumulate = 0 and left alone otherwise. */
+ * accumulate = 0 and left alone otherwise.  ws: gpt_workspace_bytes bytes.
+ * Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP. */
 int gpt_embed_bwd(const gpt_config* cfg, int B, int T, const int32_t* ids,
                   const void* dx0, float* dwte, float* dwpe, int accumulate,
                   void* ws, size_t ws_bytes, void* stream);
 
-/* Row norm of the configuration (LayerNorm with gain w and bias b, or
- * parameter-free RMSNorm): y = norm(x).  stats fp32 [2N] receives mean
- * (0 for RMSNorm) and 1/sqrt(var + eps) per row, or NULL. */
+/* Row norm of the configuration ([nanoGPT] model.py section: LayerNorm
+ * with a gain and an optional bias, the final norm before the head; [d20]
+ * Architecture row: the parameter-free RMSNorm of the nanochat form):
+ * y = norm(x) over the C entries of each of the N rows (dtype).  stats fp32
+ * [2N] receives mean (0 for RMSNorm) and 1/sqrt(var + eps) per row, or
+ * NULL.  Errors: INVALID, HIP. */
 int gpt_norm_fwd(const gpt_config* cfg, int N, const void* x, const void* w,
                  const void* b, void* y, float* stats, void* stream);
 
-/* Backward of gpt_norm_fwd: dx = dnorm(dy) (+ resid when resid != NULL),
- * dw, db fp32 [C] (accumulate 0/1; NULL for RMSNorm or no bias). */
+/* Backward of gpt_norm_fwd (same passages): dx = dnorm(dy) (+ resid when
+ * resid != NULL, the residual branch's gradient), dw, db fp32 [C]
+ * (accumulate 0/1; NULL for RMSNorm or no bias).  ws: gpt_workspace_bytes
+ * bytes (LayerNorm only).  Errors: INVALID, WORKSPACE, HIP. */
 int gpt_norm_bwd(const gpt_config* cfg, int N, const void* x, const void* w,
                  const void* dy, const void* resid, void* dx, float* dw,
                  float* db, int accumulate, void* ws, size_t ws_bytes,

@@ -192,3 +192,32 @@ def test_adamw_validation_without_gpu():
     assert call(count=1, tensors=bad) == B.GPT_ERR_INVALID
     bad[0] = B.AdamwTensorC(16, None, 48, 64, None, 4, 1)
     assert call(count=1, tensors=bad) == B.GPT_ERR_INVALID
+
+
+def test_operand_limit_refused_before_launch(L):
+    """The largest block operand, [B*T, 4C], must stay below 2 GiB (31-bit
+    buffer offsets).  A batch beyond it is refused as UNSUPPORTED by the
+    validation that runs before any launch (here without a GPU, so any launch
+    would have failed with a HIP error instead), and the sizing queries
+    return 0 for it."""
+    cfg = synth.D20_BLOCK.cfg   # C = 1280, block_size 2048: the limit falls between B = 102 and 103
+    c = B.make_config(cfg)
+    w = _weights(cfg)
+    assert 102 * 2048 * 4 * 1280 * 2 < 2 ** 31 <= 103 * 2048 * 4 * 1280 * 2
+    assert B.gpt_block_saved_bytes(c, 102, 2048) > 0
+    assert B.gpt_block_saved_bytes(c, 103, 2048) == 0
+    assert B.gpt_workspace_bytes(c, 103, 2048) == 0
+    assert _fwd(L, c, 103, 2048, w) == B.GPT_ERR_UNSUPPORTED
+    assert b"2 GiB" in L.gpt_last_error()
+    g = B.BlockGradsC(*[FAKE] * 12)
+    for f in ("ln1_w", "ln1_b", "b_qkv", "b_o", "ln2_w", "ln2_b", "b_fc", "b_proj"):
+        setattr(g, f, None)
+    assert L.gpt_block_bwd(ctypes.byref(c), 103, 2048, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, ctypes.byref(g), 0,
+                           FAKE, 1 << 40, None) == B.GPT_ERR_UNSUPPORTED
+    assert L.gpt_embed_fwd(ctypes.byref(c), 103, 2048, FAKE, FAKE, None, FAKE, None) == B.GPT_ERR_UNSUPPORTED
+    # the LM head: a logit chunk [N, 8192] bf16 reaches 2 GiB at N = 131072
+    f = L.lm_head_xent_fwd_bwd
+    assert f(ctypes.byref(c), 131072, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, None, 0, FAKE, 1 << 40, None) == \
+        B.GPT_ERR_UNSUPPORTED
+    assert f(ctypes.byref(c), 131071, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, None, 0, FAKE, 100, None) == \
+        B.GPT_ERR_WORKSPACE

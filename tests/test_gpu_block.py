@@ -142,3 +142,51 @@ def test_block_inference_matches_training_forward():
     r.forward(saved=False)
     torch.cuda.synchronize()
     assert torch.equal(y1, r.y)
+
+
+# Shapes whose grouped weight-gradient launch leaves some of its 256 blocks
+# without k-steps in the split phase (tiles left over x k-steps < 256): d20
+# at 128..320 tokens (44 leftover tiles), GPT-2 at 128 tokens (108 tiles).
+STREAMK_SPARSE = [("d20_block", 1, 128), ("d20_block", 1, 192), ("d20_block", 1, 320), ("gpt2_block", 1, 128)]
+
+
+@pytest.mark.parametrize("name,Bsz,T", STREAMK_SPARSE, ids=[f"{n}-B{b}-T{t}" for n, b, t in STREAMK_SPARSE])
+def test_block_parity_stale_workspace(name, Bsz, T):
+    """Block parity with every workspace byte set to 0xFF (NaN as fp32)
+    before the call: no result may depend on workspace contents the call did
+    not write itself."""
+    w = synth.scaled(synth.BY_NAME[name], B=Bsz, T=T)
+    print_case("block-stale-ws", name, Bsz, T)
+    x, dy, p = synth.make_block_inputs(w, random_affine=name == "gpt2_block")
+    r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
+    r.ws.fill_(255)
+    r.step()
+    torch.cuda.synchronize()
+    cfg = synth.oracle_cfg(w.cfg)
+    y_ref, cache = O.block_fwd(cfg, x, p)
+    dx_ref, g_ref = O.block_bwd(cfg, dy, cache, p)
+    rep = {}
+    assert_rel("y", to_f64(r.y).reshape(x.shape), y_ref, REL_ACT, rep)
+    assert_rel("dx", to_f64(r.dx).reshape(x.shape), dx_ref, REL_ACT, rep)
+    for k, v in g_ref.items():
+        if v is not None:
+            assert_rel("d" + k, to_f64(r.g[k]), v, REL_ACT, rep)
+    print(name, Bsz, T, {k: f"{v:.2e}" for k, v in rep.items()})
+
+
+@pytest.mark.parametrize("name,Bsz,T", [("d20_block", 1, 192), ("d20_block", 2, 2048)])
+def test_block_accumulate_streamk(name, Bsz, T):
+    """accumulate=1 through the grouped stream-K weight gradients (both the
+    whole tiles' epilogue and the fixup of the split tiles): a second
+    identical backward doubles every parameter gradient exactly (the
+    reductions have a fixed order, so the two passes are bitwise equal)."""
+    w = synth.scaled(synth.BY_NAME[name], B=Bsz, T=T)
+    print_case("block-accumulate-streamk", name, Bsz, T)
+    x, dy, p, r = _run(w, False)
+    g1 = {k: v.clone() for k, v in r.g.items() if v is not None}
+    r.ws.fill_(255)
+    r.forward()
+    r.backward(accumulate=1)
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        assert torch.equal(r.g[k], 2 * v), k

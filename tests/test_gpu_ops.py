@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _cfg(dtype="bf16", V=1000, C=64, H=4, norm="layernorm", bias=True, rope=False):
-    return synth.GPTConfig(n_layer=1, n_head=H, n_embd=C, block_size=4096, vocab_size=V, bias=bias, norm=norm,
+    return synth.GPTConfig(n_layer=1, n_head=H, n_embd=C, block_size=16384, vocab_size=V, bias=bias, norm=norm,
                            rope=rope, qk_norm=rope, dtype=dtype)
 
 
@@ -29,6 +29,10 @@ XENT = [
     ("bf16", 1000, 1280, 32768),   # 4 full chunks
     ("fp32", 64, 64, 27),
     ("fp32", 200, 64, 9000),       # two chunks, ragged
+    # the full-size heads: the GPT-2 124M step (tied, V 50304) and the d20
+    # evaluation (V 32768), N = 16384 tokens (dW and dh sum over all of them)
+    pytest.param("bf16", 16384, 768, 50304, marks=pytest.mark.timeout(900)),
+    pytest.param("bf16", 16384, 1280, 32768, marks=pytest.mark.timeout(900)),
 ]
 
 

@@ -184,3 +184,44 @@ def test_masked_xent_matches_torch():
     l0, _, dh0, _ = O.xent_fwd_bwd(h, W, y, 1.0 / N)
     assert l1 == pytest.approx(l0, rel=1e-15)
     np.testing.assert_array_equal(dh1, dh0)
+
+
+@pytest.mark.parametrize("form", ["gpt2", "d20"])
+def test_model_eval_nats_matches_torch(form):
+    """model_eval_nats, the forward-only pass of the bits-per-byte
+    evaluation, is its own code path (no caches, its own head choice and
+    final norm).  It must equal the training step's nats bit for bit, and
+    torch's per-token cross-entropy of a model built from library ops, for
+    the tied head (GPT-2 form) and the untied one (d20 form)."""
+    cfg = FORMS[form]
+    rng = np.random.default_rng(13)
+    B, T, C, V, L = 2, 12, 32, 31, 2
+    ids = rng.integers(0, V, (B, T))
+    y = rng.integers(0, V, (B, T))
+    ln = cfg["norm"] == "layernorm"
+    P = {"wte": 0.3 * rng.standard_normal((V, C)),
+         "wpe": None if cfg["rope"] else 0.3 * rng.standard_normal((T, C)),
+         "blocks": [_params(rng, C, cfg) for _ in range(L)],
+         "lnf_w": 1 + 0.1 * rng.standard_normal(C) if ln else None,
+         "lnf_b": 0.1 * rng.standard_normal(C) if ln else None,
+         "lm_head": None if form == "gpt2" else 0.3 * rng.standard_normal((V, C))}
+    nats = O.model_eval_nats(cfg, ids, y, P)
+    _, nats_step, _ = O.model_fwd_bwd(cfg, ids, y, P, want_grad=False)
+    np.testing.assert_array_equal(nats, nats_step)
+    with torch.no_grad():
+        x = F.embedding(torch.tensor(ids), torch.tensor(P["wte"]))
+        if P["wpe"] is not None:
+            x = x + torch.tensor(P["wpe"])[None]
+        for bp in P["blocks"]:
+            x = _torch_block(cfg, x, {k: None if v is None else torch.tensor(v) for k, v in bp.items()})
+        if ln:
+            h = F.layer_norm(x, (C,), torch.tensor(P["lnf_w"]), torch.tensor(P["lnf_b"]), cfg["eps"])
+        else:
+            h = F.rms_norm(x, (C,), None, cfg["eps"])
+        head = torch.tensor(P["lm_head"] if P["lm_head"] is not None else P["wte"])
+        nt = F.cross_entropy(F.linear(h, head).reshape(-1, V), torch.tensor(y).reshape(-1), reduction="none")
+    assert _rel(nats, nt.numpy()) < 1e-12
+    # the head choice matters: the other weight gives different nats
+    if P["lm_head"] is not None:
+        P2 = dict(P, lm_head=None)
+        assert _rel(O.model_eval_nats(cfg, ids, y, P2), nt.numpy()) > 1e-3
