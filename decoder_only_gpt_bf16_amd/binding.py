@@ -76,6 +76,7 @@ _SIGS = {
     "gpt_norm_bwd": (_I, [_CFG, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _VP, _SZ, _VP]),
     "gpt_adamw_step": (_I, [ctypes.POINTER(AdamwConfigC), _ATP, _I, _VP, _VP, _SZ, _VP]),
     "gpt_adamw_workspace_bytes": (_SZ, [_ATP, _I]),
+    "gpt_adamw_step_noalloc": (_I, [ctypes.POINTER(AdamwConfigC), _ATP, _I, _VP, _VP]),
     "gpt_fp8_quantize": (_I, [ctypes.c_int64, _VP, _I, _VP, _VP, _VP, _SZ, _VP]),
     "gpt_fp8_workspace_bytes": (_SZ, [ctypes.c_int64]),
     "gpt_fp8_gemm": (_I, [_I, _I, _I, _VP, ctypes.c_int64, _I, _VP, _VP, ctypes.c_int64, _I, _VP, _VP,
@@ -277,6 +278,15 @@ def gpt_adamw_step(tensors, lr, beta1, beta2, eps, weight_decay, step, max_norm,
     _check(lib().gpt_adamw_step(ctypes.byref(cfg), arr, len(arr), _p(grad_norm, "f32"), _p(ws), _nbytes(ws),
                                 _stream(stream)))
 
+
+def gpt_adamw_step_noalloc(tensors, lr, beta1, beta2, eps, weight_decay, step, max_norm, grad_norm, stream=None):
+    """gpt_adamw_step with the library's own per-GPU scratch (no workspace)."""
+    arr = _adamw_table(tensors)
+    cfg = AdamwConfigC(lr, beta1, beta2, eps, weight_decay, int(step), max_norm)
+    _check(lib().gpt_adamw_step_noalloc(ctypes.byref(cfg), arr, len(arr), _p(grad_norm, "f32"), _stream(stream)))
+
+
+ADAMW_NOALLOC_MAX_CHUNKS = 131072
 
 FP8_E4M3, FP8_E5M2 = 0, 1
 

@@ -2,6 +2,7 @@
 // saved-activation and workspace planning, and the launch sequence of each
 // entry point on the caller's stream.  No allocation, no synchronisation.
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -700,9 +701,19 @@ int gpt_fp8_gemm(int M, int N, int K, const void* qa, int64_t lda, int fmt_a, co
 }
 
 // ------------------------------------------------------------ optimizer
-static int adamw_tensors(const gpt_adamw_tensor* tensors, int count, std::vector<OptTensor>& out) {
+// The C descriptor and the kernels' one share their layout, so the caller's
+// array is read in place (no copy, no allocation).
+static_assert(sizeof(gpt_adamw_tensor) == sizeof(OptTensor), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, param) == offsetof(OptTensor, p), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, grad) == offsetof(OptTensor, g), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, m) == offsetof(OptTensor, m), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, v) == offsetof(OptTensor, v), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, param_bf16) == offsetof(OptTensor, p16), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, n) == offsetof(OptTensor, n), "descriptor layouts differ");
+static_assert(offsetof(gpt_adamw_tensor, decay) == offsetof(OptTensor, decay), "descriptor layouts differ");
+
+static int adamw_tensors(const gpt_adamw_tensor* tensors, int count, const OptTensor** out) {
   if (!tensors || count <= 0) return fail(GPT_ERR_INVALID, "no tensors");
-  out.resize(count);
   for (int i = 0; i < count; ++i) {
     const gpt_adamw_tensor& t = tensors[i];
     if (!t.param || !t.grad || !t.m || !t.v) return fail(GPT_ERR_INVALID, "tensor %d: a pointer is NULL", i);
@@ -710,19 +721,12 @@ static int adamw_tensors(const gpt_adamw_tensor* tensors, int count, std::vector
     if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.m) || !aligned16(t.v) ||
         !aligned16(t.param_bf16))
       return fail(GPT_ERR_INVALID, "tensor %d: pointer not 16-byte aligned", i);
-    out[i] = OptTensor{t.param, t.grad, t.m, t.v, t.param_bf16, (long)t.n, t.decay ? 1 : 0};
   }
+  *out = reinterpret_cast<const OptTensor*>(tensors);
   return GPT_OK;
 }
 
-size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count) {
-  std::vector<OptTensor> t;
-  if (adamw_tensors(tensors, count, t)) return 0;
-  return adamw_ws_bytes(t.data(), count);
-}
-
-int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors, int count, float* grad_norm,
-                   void* ws, size_t ws_bytes, void* stream) {
+static int adamw_config(const gpt_adamw_config* cfg) {
   if (!cfg) return fail(GPT_ERR_INVALID, "cfg is NULL");
   const float hp[] = {cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, cfg->max_norm};
   for (float x : hp)
@@ -733,16 +737,49 @@ int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors,
   if (cfg->eps < 0.0f || cfg->lr < 0.0f || cfg->weight_decay < 0.0f)
     return fail(GPT_ERR_INVALID, "lr, eps and weight_decay must be non-negative");
   if (cfg->eps == 0.0f && cfg->beta2 == 0.0f) return fail(GPT_ERR_INVALID, "eps = 0 needs beta2 > 0");
-  std::vector<OptTensor> t;
-  int st = adamw_tensors(tensors, count, t);
+  return GPT_OK;
+}
+
+size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count) {
+  const OptTensor* t = nullptr;
+  if (adamw_tensors(tensors, count, &t)) return 0;
+  return adamw_ws_bytes(t, count);
+}
+
+int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors, int count, float* grad_norm,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int st = adamw_config(cfg);
   if (st) return st;
-  if (adamw_chunks(t.data(), count) > (1L << 30)) return fail(GPT_ERR_UNSUPPORTED, "parameter set too large");
-  const size_t need = adamw_ws_bytes(t.data(), count);
+  const OptTensor* t = nullptr;
+  if ((st = adamw_tensors(tensors, count, &t))) return st;
+  if (adamw_chunks(t, count) > (1L << 30)) return fail(GPT_ERR_UNSUPPORTED, "parameter set too large");
+  const size_t need = adamw_ws_bytes(t, count);
   if (!ws || ws_bytes < need) return fail(GPT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
   if (!aligned16(ws) || !aligned16(grad_norm)) return fail(GPT_ERR_INVALID, "ws or grad_norm not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  RUN("adamw", launch_adamw(t.data(), count, cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
+  RUN("adamw", launch_adamw(t, count, cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
                             cfg->step, cfg->max_norm, grad_norm, ws, s));
+  return GPT_OK;
+}
+
+int gpt_adamw_step_noalloc(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors, int count,
+                           float* grad_norm, void* stream) {
+  int st = adamw_config(cfg);
+  if (st) return st;
+  const OptTensor* t = nullptr;
+  if ((st = adamw_tensors(tensors, count, &t))) return st;
+  const long chunks = adamw_chunks(t, count);
+  if (chunks > ADAMW_NOALLOC_MAX_CHUNKS)
+    return fail(GPT_ERR_UNSUPPORTED, "%ld chunks of 8192 elements exceed the %ld of the built-in scratch", chunks,
+                ADAMW_NOALLOC_MAX_CHUNKS);
+  if (!aligned16(grad_norm)) return fail(GPT_ERR_INVALID, "grad_norm not 16-byte aligned");
+  void* scr = nullptr;
+  HIPCHK(adamw_noalloc_scratch(&scr));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // every partial and the clip factor the kernels read are written first by
+  // this same call, so nothing in the scratch needs clearing
+  RUN("adamw", launch_adamw(t, count, cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
+                            cfg->step, cfg->max_norm, grad_norm, scr, s));
   return GPT_OK;
 }
 

@@ -208,6 +208,11 @@ size_t adamw_ws_bytes(const OptTensor* t, int count);
 hipError_t launch_adamw(const OptTensor* t, int count, float lr, float beta1, float beta2, float eps,
                         float weight_decay, int step, float max_norm, float* norm_out, void* ws,
                         hipStream_t s);
+// The allocation-free variant's scratch: a device array of this many chunk
+// partials (plus 256 bytes) per GPU; adamw_noalloc_scratch gives its address
+// on the current device.
+constexpr long ADAMW_NOALLOC_MAX_CHUNKS = 131072;
+hipError_t adamw_noalloc_scratch(void** ptr);
 
 // FP8 (fp8.hip).  Formats: OCP E4M3 and E5M2.
 constexpr int FP8_E4M3 = 0, FP8_E5M2 = 1;

@@ -18,8 +18,18 @@
 // kernel arguments; larger sets take several launches.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kernels.h"
+
+// Scratch of the allocation-free entry point (gpt_adamw_step_noalloc): the
+// fp64 gradient-norm partial of each chunk, then the clip factor and the
+// norm, laid out as launch_adamw lays out its workspace.  A file-scope
+// device array: every GPU the library runs on holds its own copy until the
+// process ends.  In host code the name is only a stand-in for the symbol;
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device (adamw_noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[ADAMW_NOALLOC_MAX_CHUNKS * sizeof(double) + 256];
 
 namespace {
 
@@ -242,5 +252,26 @@ hipError_t launch_adamw(const OptTensor* t, int count, float lr, float beta1, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return hipSuccess;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for the process.
+hipError_t adamw_noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
   return hipSuccess;
 }

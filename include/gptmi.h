@@ -230,6 +230,22 @@ int gpt_adamw_step(const gpt_adamw_config* cfg, const gpt_adamw_tensor* tensors,
                    void* stream);
 size_t gpt_adamw_workspace_bytes(const gpt_adamw_tensor* tensors, int count);
 
+/* gpt_adamw_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc): the same update and results, with no workspace argument.  Its
+ * scratch is a device array inside the library of GPT_ADAMW_NOALLOC_MAX_CHUNKS
+ * fp64 partials plus 256 bytes (1 MiB), one copy per GPU, held until the
+ * process ends; the call makes no hipMalloc, hipFree or other allocation.
+ * Capacity: the sum over tensors of ceil(n / 8192) must not exceed
+ * GPT_ADAMW_NOALLOC_MAX_CHUNKS (up to 2^30 parameters); larger sets return
+ * UNSUPPORTED.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (concurrent streams, threads) race and must be
+ * serialized by the caller.  Errors: INVALID, UNSUPPORTED, HIP. */
+#define GPT_ADAMW_NOALLOC_MAX_CHUNKS 131072
+int gpt_adamw_step_noalloc(const gpt_adamw_config* cfg,
+                           const gpt_adamw_tensor* tensors, int count,
+                           float* grad_norm, void* stream);
+
 /* ---- FP8 GEMMs ---- */
 
 #define GPT_FP8_E4M3 0   /* OCP E4M3: bias 7, largest finite 448, no infinities */
