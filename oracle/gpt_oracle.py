@@ -31,6 +31,7 @@ __all__ = [
     "xent_fwd_bwd", "val_bpb", "model_fwd_bwd", "model_eval_nats",
     "norm_fwd", "norm_bwd", "clip_scale", "adamw_step",
     "FP8_FORMATS", "fp8_round", "fp8_encode", "fp8_quantize", "fp8_gemm",
+    "bf16_round", "fp8_linear_fwd", "fp8_linear_bwd",
 ]
 
 
@@ -185,6 +186,54 @@ def linear_bwd(dy, x, w, has_bias):
     return dx, dw, db
 
 
+_linear_fwd, _linear_bwd = linear_fwd, linear_bwd
+
+
+def bf16_round(x):
+    """Nearest bfloat16 value (8 significant bits, ties to even) of each
+    element, through float32 (itself rounded to nearest even)."""
+    bits = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    keep = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return keep.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# FP8 Linear layers ("Train your own ChatGPT", 6.2, FP8 paragraph: per-tensor
+# dynamic scales, E4M3 for activations and weights, E5M2 for gradients, and
+# both backward matmuls in FP8 as well).  Reading: the quantized operand of
+# an activation or gradient is the bf16 value its storage holds (activations
+# and activation gradients are bf16 tensors), then quantized by
+# fp8_quantize; the bias and its gradient stay in full precision.
+
+def _q(x, fmt):
+    return fp8_quantize(bf16_round(x), fmt)
+
+
+def fp8_linear_fwd(x, w, b):
+    """y = x W^T + b with x and W quantized to E4M3, each with its own scale."""
+    K = x.shape[-1]
+    qx, sx, _ = _q(x.reshape(-1, K), "e4m3")
+    qw, sw, _ = _q(w, "e4m3")
+    y = fp8_gemm(qx, sx, qw, sw).reshape(x.shape[:-1] + (w.shape[0],))
+    if b is not None:
+        y = y + b
+    return y
+
+
+def fp8_linear_bwd(dy, x, w, has_bias):
+    """dx = q(dy) q(W) and dW = q(dy)^T q(x), dy in E5M2, W and x in E4M3
+    (the same codes as the forward's); db = column sums of dy."""
+    K = x.shape[-1]
+    O = dy.shape[-1]
+    dy2 = dy.reshape(-1, O)
+    qg, sg, _ = _q(dy2, "e5m2")
+    qw, sw, _ = _q(w, "e4m3")
+    qx, sx, _ = _q(x.reshape(-1, K), "e4m3")
+    dx = fp8_gemm(qg, sg, qw.T, sw).reshape(x.shape)
+    dw = fp8_gemm(qg.T, sg, qx.T, sx)
+    db = dy2.sum(axis=0) if has_bias else None
+    return dx, dw, db
+
+
 # ----------------------------------------------------------------------------
 # Causal self-attention (nanoGPT page, CausalSelfAttention paragraph: the
 # explicit lower-triangular mask blocks attention to future positions).
@@ -269,12 +318,14 @@ def _heads(x, H):
 
 def block_fwd(cfg, x, p):
     """x: [B, T, C]; p: dict of block parameters (None where absent).
+    cfg["fp8"] true: the four Linear layers run in FP8 (fp8_linear_fwd).
 
     Returns (y, cache) where cache holds what block_bwd needs.
     """
     H = cfg["n_head"]
     C = x.shape[-1]
     bias = cfg["bias"]
+    linear_fwd = fp8_linear_fwd if cfg.get("fp8") else _linear_fwd
     a1 = norm_fwd(cfg, x, p.get("ln1_w"), p.get("ln1_b"))
     qkv = linear_fwd(a1, p["w_qkv"], p.get("b_qkv") if bias else None)
     q, k, v = _heads(qkv[..., :C], H), _heads(qkv[..., C:2 * C], H), _heads(qkv[..., 2 * C:], H)
@@ -298,9 +349,11 @@ def block_fwd(cfg, x, p):
 
 
 def block_bwd(cfg, dy, cache, p):
-    """Backward of block_fwd.  Returns (dx, grads dict with the same keys as p)."""
+    """Backward of block_fwd (FP8 Linear backward with cfg["fp8"]).
+    Returns (dx, grads dict with the same keys as p)."""
     H = cfg["n_head"]
     bias = cfg["bias"]
+    linear_bwd = fp8_linear_bwd if cfg.get("fp8") else _linear_bwd
     x, x1 = cache["x"], cache["x1"]
     grads = {}
     # MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
