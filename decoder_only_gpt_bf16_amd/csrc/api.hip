@@ -580,8 +580,7 @@ static int xent_impl(const gpt_config* cfg, int N, const void* h, const void* W,
   const int C = d.C, V = d.V, ty = d.dtype;
   float* nt = nats ? nats : x.nats;
   const bool mfma = ty == 1;
-  // a target outside [0, V) matches no column and leaves NaN in its nats
-  RUN("xent_fill", launch_fill_f32(x.ztgt, N, __builtin_nanf(""), s));
+  // a target outside [0, V) matches no column: xent_finish gives it NaN nats
   for (int c = 0; c < x.nchunk; ++c) {
     const int v0 = c * x.Vc;
     const int Vw = std::min(x.Vc, V - v0);
@@ -601,8 +600,8 @@ static int xent_impl(const gpt_config* cfg, int N, const void* h, const void* W,
       RUN("xent_rows_stats", launch_xent_rows_stats(N, Vw, v0, x.zbuf, x.ldz, targets, x.run, x.ztgt, c == 0, s));
     }
   }
-  RUN("xent_finish",
-      launch_xent_finish(N, mfma ? x.P : 1, mfma ? x.part : x.run, x.ztgt, weight, x.lse, nt, x.loss_part, s));
+  RUN("xent_finish", launch_xent_finish(N, mfma ? x.P : 1, V, mfma ? x.part : x.run, targets, x.ztgt, weight, x.lse,
+                                        nt, x.loss_part, s));
   RUN("loss_sum", launch_loss_sum(xent_finish_blocks(N), x.loss_part, loss_scale, loss, s));
   if (!dh && !dW) return GPT_OK;
   for (int c = 0; c < x.nchunk; ++c) {

@@ -168,11 +168,12 @@ hipError_t launch_attn_bwd_dq(int dtype, int B, int T, int H, int D, int window,
 bool attn_mfma_supported(int dtype, int D);
 
 // Cross-entropy reductions.
-// Combine per-row partials into lse, nats = lse - ztgt, block loss partials.
+// Combine per-row partials into lse, nats = lse - ztgt (NaN for a target
+// outside [0, V), whose ztgt no chunk wrote), block loss partials.
 // w (optional): per-token weights of the loss sum; a token of weight 0
 // contributes nothing (also when its target is out of range).
-hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, const float* w, float* lse,
-                              float* nats, float* loss_part, hipStream_t s);
+hipError_t launch_xent_finish(int N, int P, int V, const float2* part, const int32_t* tgt, const float* ztgt,
+                              const float* w, float* lse, float* nats, float* loss_part, hipStream_t s);
 hipError_t launch_loss_sum(int nblk, const float* loss_part, float scale, float* loss,
                            hipStream_t s);
 int xent_finish_blocks(int N);
@@ -184,7 +185,6 @@ hipError_t launch_xent_rows_grad(int dtype, int N, int Vc, int v0, const float* 
                                  const int32_t* tgt, const float* lse, float scale, const float* w, void* dz,
                                  long lddz, hipStream_t s);
 hipError_t launch_f32_to(int dtype, long n, const float* src, void* dst, hipStream_t s);
-hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t s);
 
 // targets outside [0, V) count as zero-byte tokens.
 hipError_t launch_bpb(int N, int V, const float* nats, const int32_t* targets, const int32_t* token_bytes,

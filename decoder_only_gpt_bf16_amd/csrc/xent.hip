@@ -24,9 +24,16 @@ __device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
   m = mn;
 }
 
-// One wave per row: merge P partials -> lse; nats = lse - ztgt.  Per-block
-// sum of nats into loss_part[block] (waves in fixed order).
-__global__ __launch_bounds__(256) void xent_finish_k(int N, int P, const float2* __restrict__ part,
+// One wave per row: lse from the row's P (max, sum exp) partials, nats =
+// lse - z[target] (NaN when the target lies outside [0, V): no tile wrote its
+// logit).  Per-block sum of the (weighted) nats into loss_part[block] (waves
+// in fixed order).  A lane takes partials lane, lane + 64, ... in batches of
+// XB with all of a batch's loads issued before any arithmetic, and folds
+// each batch into its (max, sum) with one exponential per partial.
+constexpr int XB = 16;
+
+__global__ __launch_bounds__(256) void xent_finish_k(int N, int P, int V, const float2* __restrict__ part,
+                                                     const int32_t* __restrict__ tgt,
                                                      const float* __restrict__ ztgt, const float* __restrict__ w,
                                                      float* __restrict__ lse, float* __restrict__ nats,
                                                      float* __restrict__ loss_part) {
@@ -35,10 +42,25 @@ __global__ __launch_bounds__(256) void xent_finish_k(int N, int P, const float2*
   const int row = blockIdx.x * FINISH_ROWS + wave;
   float nat = 0.0f;
   if (row < N) {
+    const float2* pr = part + (long)row * P;
     float m = -INFINITY, s = 0.0f;
-    for (int p = lane; p < P; p += 64) {
-      const float2 v = part[(long)row * P + p];
-      merge(m, s, v.x, v.y);
+    for (int p0 = 0; p0 < P; p0 += 64 * XB) {
+      float2 v[XB];
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        const int p = p0 + lane + 64 * i;
+        v[i] = p < P ? pr[p] : make_float2(-INFINITY, 0.0f);
+      }
+      float mb = m;
+#pragma unroll
+      for (int i = 0; i < XB; ++i) mb = fmaxf(mb, v[i].x);
+      if (mb != -INFINITY) {
+        float sb = s * expf(m - mb);
+#pragma unroll
+        for (int i = 0; i < XB; ++i) sb = fmaf(v[i].y, expf(v[i].x - mb), sb);
+        m = mb;
+        s = sb;
+      }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -46,7 +68,8 @@ __global__ __launch_bounds__(256) void xent_finish_k(int N, int P, const float2*
       merge(m, s, m2, s2);
     }
     const float l = m + logf(s);
-    nat = l - ztgt[row];
+    const int t = tgt[row];
+    nat = (t >= 0 && t < V) ? l - ztgt[row] : __builtin_nanf("");
     if (lane == 0) {
       lse[row] = l;
       nats[row] = nat;
@@ -123,10 +146,6 @@ __global__ void f32_to_k(long n, const float* __restrict__ src, T* __restrict__ 
     dst[i] = from_f32<T>(src[i]);
 }
 
-__global__ void fill_f32_k(long n, float* p, float v) {
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = v;
-}
-
 __global__ __launch_bounds__(1024) void bpb_k(int N, int V, const float* __restrict__ nats, const int32_t* __restrict__ tg,
                                               const int32_t* __restrict__ tb, double* __restrict__ sum_nats,
                                               int64_t* __restrict__ sum_bytes) {
@@ -162,10 +181,10 @@ __global__ __launch_bounds__(1024) void bpb_k(int N, int V, const float* __restr
 
 int xent_finish_blocks(int N) { return cdiv(N, FINISH_ROWS); }
 
-hipError_t launch_xent_finish(int N, int P, const float2* part, const float* ztgt, const float* w, float* lse,
-                              float* nats, float* loss_part, hipStream_t s) {
-  hipLaunchKernelGGL(xent_finish_k, dim3(xent_finish_blocks(N)), dim3(256), 0, s, N, P, part, ztgt, w, lse, nats,
-                     loss_part);
+hipError_t launch_xent_finish(int N, int P, int V, const float2* part, const int32_t* tgt, const float* ztgt,
+                              const float* w, float* lse, float* nats, float* loss_part, hipStream_t s) {
+  hipLaunchKernelGGL(xent_finish_k, dim3(xent_finish_blocks(N)), dim3(256), 0, s, N, P, V, part, tgt, ztgt, w, lse,
+                     nats, loss_part);
   return hipGetLastError();
 }
 
@@ -196,11 +215,6 @@ hipError_t launch_f32_to(int dtype, long n, const float* src, void* dst, hipStre
   dim3 grid((unsigned)std::min<long>(cdiv(n, 256), 8192));
   if (dtype == 1) hipLaunchKernelGGL(f32_to_k<bf16>, grid, dim3(256), 0, s, n, src, (bf16*)dst);
   else hipLaunchKernelGGL(f32_to_k<float>, grid, dim3(256), 0, s, n, src, (float*)dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t s) {
-  hipLaunchKernelGGL(fill_f32_k, dim3((unsigned)std::min<long>(cdiv(n, 256), 4096)), dim3(256), 0, s, n, p, v);
   return hipGetLastError();
 }
 
