@@ -172,7 +172,7 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="also time the d20 block with sliding-window attention of this many keys")
     ap.add_argument("--fp8", action="store_true",
-                    help="also time FP8 quantization and FP8 GEMMs at the d20 Linear shapes")
+                    help="also time FP8 quantization, FP8 GEMMs at the d20 Linear shapes and the FP8 d20 block step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     args = ap.parse_args()
@@ -264,6 +264,7 @@ def main():
             out["extra"][f"d20_block_window{args.window}"] = window_workload(args, args.window)
         if args.fp8:
             out["extra"]["fp8_d20_linears"] = fp8_workload(args)
+            out["extra"]["fp8_d20_block"] = fp8_block_workload(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
@@ -302,6 +303,35 @@ def window_workload(args, window):
 
 
 PEAK_FP8 = 5.0e15        # MI355X dense fp8 MFMA
+
+
+def fp8_block_workload(args):
+    """The d20 block fwd+bwd with its four Linear layers as FP8 GEMMs
+    (gpt_config.fp8: activations and weights E4M3, gradients E5M2, dynamic
+    per-tensor scales), the same useful FLOPs as the bf16 step; priced
+    against the bf16 peak like the headline (the FP8 share is its GEMMs)."""
+    import torch
+    from decoder_only_gpt_bf16_amd import binding as B
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import BlockRunner
+    w = synth.scaled(synth.D20_BLOCK, fp8=True)
+    cfg = w.cfg
+    x, dy, p = synth.make_block_inputs(w)
+    r = BlockRunner(cfg, w.B, w.T, x, dy, p)
+    per = []
+    ms = time_steps(r.step, args.steps, args.warmup, per)
+    B.gpt_trace_begin(128 * args.steps)
+    for _ in range(args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    trace = B.gpt_trace_end()
+    f = block_flops(w.B, w.T, cfg.n_embd, cfg.n_head)
+    del r
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1), "ms": round(ms, 4),
+            "ms_median": round(sorted(per)[len(per) // 2], 4), "bf16_peak_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4),
+            "sites_us": {k: round(v[1] / v[0], 2) for k, v in trace.items()},
+            "launches_per_step": {k: v[0] / args.steps for k, v in trace.items()}}
 
 
 def fp8_workload(args):

@@ -32,7 +32,7 @@ class GptConfigC(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("vocab_size", ctypes.c_int32), ("bias", ctypes.c_int32),
                 ("norm", ctypes.c_int32), ("rope", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("attn_window", ctypes.c_int32)]
+                ("attn_window", ctypes.c_int32), ("fp8", ctypes.c_int32)]
 
 
 class BlockWeightsC(ctypes.Structure):
@@ -119,7 +119,7 @@ def make_config(cfg) -> GptConfigC:
     return GptConfigC(cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.block_size, cfg.vocab_size, int(cfg.bias),
                       0 if cfg.norm == "layernorm" else 1, int(cfg.rope), int(cfg.qk_norm),
                       float(cfg.rope_base), float(cfg.eps), 1 if cfg.dtype == "bf16" else 0,
-                      int(getattr(cfg, "window", 0)))
+                      int(getattr(cfg, "window", 0)), int(getattr(cfg, "fp8", False)))
 
 
 def _p(t, want=None) -> Optional[int]:

@@ -115,6 +115,8 @@ int check_cfg(const gpt_config* cfg, Dims& d) {
   if (cfg->rope && (d.D & 1)) return fail(GPT_ERR_INVALID, "odd head_dim %d with rope", d.D);
   if (cfg->rope && !(cfg->rope_base > 0.0f)) return fail(GPT_ERR_INVALID, "rope_base must be > 0");
   if (d.D % 8 || d.D > 128) return fail(GPT_ERR_UNSUPPORTED, "head_dim %d not a multiple of 8 in [8, 128]", d.D);
+  if (cfg->fp8 && (cfg->dtype != GPT_DTYPE_BF16 || d.C % 16))
+    return fail(GPT_ERR_UNSUPPORTED, "fp8 needs bf16 storage and n_embd %% 16 == 0");
   if (d.C > 2048) return fail(GPT_ERR_UNSUPPORTED, "n_embd %d > 2048", d.C);
   return GPT_OK;
 }
@@ -142,7 +144,16 @@ struct Saved {
   float2* cs;                            // RoPE (cos, sin) table [T][D/2], written by the forward
   void *a1, *qkv, *o, *x1, *a2, *u, *g;  // u holds GELU'(fc output), g = GELU(fc output)
   float *stats1, *stats2, *qkr, *lse;
+  // FP8 (cfg->fp8): per-tensor quantizer scales [8][4] of a1, W_qkv, o, W_o,
+  // a2, W_fc, g, W_proj; transposed codes of those activations [In][Np] and
+  // weights [In][Out] for the backward's GEMMs
+  float* f8sc;
+  uint8_t *qa1T, *qoT, *qa2T, *qgT, *qWqkvT, *qWoT, *qWfcT, *qWprojT;
 };
+
+// tokens padded to whole 64-row tiles of the transposed codes
+long fp8_np(long N) { return (N + 63) / 64 * 64; }
+long fp8_ld64(long n) { return (n + 63) / 64 * 64; }
 
 Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   Saved s{};
@@ -159,13 +170,44 @@ Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   s.stats2 = a.take_n<float>(2 * N);
   s.u = a.take(N * 4 * C * es);
   s.g = a.take(N * 4 * C * es);
+  if (cfg->fp8) {
+    const size_t Np = fp8_np(N);
+    s.f8sc = a.take_n<float>(32);
+    s.qa1T = a.take_n<uint8_t>(C * Np);
+    s.qoT = a.take_n<uint8_t>(C * Np);
+    s.qa2T = a.take_n<uint8_t>(C * Np);
+    s.qgT = a.take_n<uint8_t>(4 * C * Np);
+    s.qWqkvT = a.take_n<uint8_t>(C * fp8_ld64(3 * C));
+    s.qWoT = a.take_n<uint8_t>(C * fp8_ld64(C));
+    s.qWfcT = a.take_n<uint8_t>(C * fp8_ld64(4 * C));
+    s.qWprojT = a.take_n<uint8_t>(4 * C * fp8_ld64(C));
+  }
   return s;
+}
+
+// FP8 forward temporaries: codes of the current Linear's activation and
+// weight, amax partials
+struct Fp8FwdWs {
+  uint8_t *qx, *qw;
+  float* part;
+};
+Fp8FwdWs fp8_fwd_layout(const Dims& d, Arena& a) {
+  Fp8FwdWs f{};
+  const size_t N = d.N, C = d.C;
+  f.qx = a.take_n<uint8_t>(N * 4 * C);
+  f.qw = a.take_n<uint8_t>(4 * C * C);
+  f.part = a.take_n<float>(std::max(fp8_amax_parts((long)N * 4 * C), fp8_amax_parts(4L * C * C)));
+  return f;
 }
 
 struct BwdWs {
   void *du, *da, *dx1, *dO, *dqkv;
   float *delta, *colpart, *colsum, *split;
   void *wt_fc, *wt_o, *wt_qkv;  // bf16: transposed weights for the input gradients
+  // FP8: codes of the current gradient [N][Out] and their transpose
+  // [Out][Np], amax partials, the gradients' scales [4][4]
+  uint8_t *qg, *qgT;
+  float *f8part, *f8sc;
 };
 
 GemmDesc gemm0() {
@@ -218,10 +260,30 @@ void block_wgrads(const Dims& d, GemmDesc* wg) {
   wg[3] = lin_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0);   // qkv
 }
 
-size_t split_need(const Dims& d) {
+// FP8 weight gradient dW[Out, In] = q(dY)^T q(X): both operands transposed
+// codes [.][Np], k = tokens
+GemmDesc fp8_wgrad(const Dims& d, const void* qdyT, int Out, const void* qxT, int In, float* dW, int accumulate) {
+  GemmDesc g = gemm0();
+  const long Np = fp8_np(d.N);
+  g.A = qdyT; g.lda = Np; g.B = qxT; g.ldb = Np;
+  g.M = Out; g.N = In; g.K = (int)Np; g.epi = EPI_F32;
+  g.out = dW; g.ldc = In; g.accumulate = accumulate;
+  return g;
+}
+
+size_t split_need(const Dims& d, const gpt_config* cfg) {
   GemmDesc wg[4];
   block_wgrads(d, wg);
-  return gemm_group_scratch_bytes(wg, 4, d.dtype);
+  size_t need = gemm_group_scratch_bytes(wg, 4, d.dtype);
+  if (cfg->fp8) {
+    const int C = d.C;
+    const GemmDesc f[4] = {fp8_wgrad(d, nullptr, C, nullptr, 4 * C, nullptr, 0),
+                           fp8_wgrad(d, nullptr, 4 * C, nullptr, C, nullptr, 0),
+                           fp8_wgrad(d, nullptr, C, nullptr, C, nullptr, 0),
+                           fp8_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0)};
+    for (const GemmDesc& g : f) need = std::max(need, gemm_fp8_split_scratch_bytes(g));
+  }
+  return need;
 }
 
 BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
@@ -235,11 +297,17 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   w.delta = a.take_n<float>((size_t)d.B * d.H * d.T);
   w.colpart = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
   w.colsum = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, 4 * C)));
-  w.split = static_cast<float*>(a.take(split_need(d)));
-  if (d.dtype == GPT_DTYPE_BF16) {
+  w.split = static_cast<float*>(a.take(split_need(d, cfg)));
+  if (d.dtype == GPT_DTYPE_BF16 && !cfg->fp8) {
     w.wt_fc = a.take(4 * C * C * es);
     w.wt_o = a.take(C * C * es);
     w.wt_qkv = a.take(3 * C * C * es);
+  }
+  if (cfg->fp8) {
+    w.qg = a.take_n<uint8_t>(N * 4 * C);
+    w.qgT = a.take_n<uint8_t>(4 * C * fp8_np(N));
+    w.f8part = a.take_n<float>(fp8_amax_parts((long)N * 4 * C));
+    w.f8sc = a.take_n<float>(16);
   }
   return w;
 }
@@ -247,6 +315,7 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
 size_t fwd_ws_bytes(const Dims& d, const gpt_config* cfg, bool inference) {
   Arena a(nullptr);
   if (inference) saved_layout(d, cfg, a);
+  if (cfg->fp8) fp8_fwd_layout(d, a);
   return a.used();
 }
 
@@ -424,6 +493,30 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   Saved sv = saved_layout(d, cfg, sa);
   float2* cs = sv.cs;
   const int C = d.C, ty = d.dtype, kind = cfg->norm;
+  Arena fa = saved ? Arena(ws) : sa;  // FP8 temporaries follow the intermediates
+  const Fp8FwdWs fw = cfg->fp8 ? fp8_fwd_layout(d, fa) : Fp8FwdWs{};
+
+  // One Linear layer: the bf16 GEMM, or with cfg->fp8 the activation and the
+  // weight quantized to E4M3 (their transposed codes kept in `saved` for the
+  // backward) and the FP8 GEMM with the same epilogue.  slot: the
+  // activation's scale slot in sv.f8sc, the weight's is slot + 1.
+  auto linear = [&](const char* name, GemmDesc g, int slot, uint8_t* qxT, uint8_t* qwT) -> int {
+    if (!cfg->fp8) {
+      RUN(name, launch_gemm(g, ty, nullptr, s));
+      return GPT_OK;
+    }
+    const int In = g.K, Out = g.N;
+    float* sx = sv.f8sc + 4 * slot;
+    float* sw = sv.f8sc + 4 * (slot + 1);
+    RUN("fp8_quant_w", launch_fp8_quantize_2d(Out, In, g.B, FP8_E4M3, fw.qw, saved ? qwT : nullptr,
+                                              fp8_ld64(Out), sw, fw.part, s));
+    RUN("fp8_quant_x", launch_fp8_quantize_2d(d.N, In, g.A, FP8_E4M3, fw.qx, saved ? qxT : nullptr, fp8_np(d.N),
+                                              sx, fw.part, s));
+    g.A = fw.qx; g.lda = In; g.B = fw.qw; g.ldb = In;
+    g.f8_sa = sx; g.f8_sb = sw;
+    RUN(name, launch_gemm_fp8(g, 1, nullptr, s));
+    return GPT_OK;
+  };
 
   if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, cs, s));
   RUN("norm1_fwd", launch_norm_fwd(ty, kind, d.N, C, x, w->ln1_w, opt(cfg, w->ln1_b), cfg->norm_eps, sv.a1, sv.stats1, s));
@@ -437,21 +530,21 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
     g.qk_cs = cs; g.qk_rstd = sv.qkr; g.qk_T = T; g.qk_rope = cfg->rope; g.qk_norm = cfg->qk_norm;
     g.qk_eps = cfg->norm_eps;
   }
-  RUN("qkv_gemm", launch_gemm(g, ty, nullptr, s));
+  if ((st = linear("qkv_gemm", g, 0, sv.qa1T, sv.qWqkvT))) return st;
   if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
   RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, cfg->attn_window, sv.qkv, sv.o, sv.lse, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
   g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
-  RUN("out_gemm", launch_gemm(g, ty, nullptr, s));
+  if ((st = linear("out_gemm", g, 2, sv.qoT, sv.qWoT))) return st;
   RUN("norm2_fwd", launch_norm_fwd(ty, kind, d.N, C, sv.x1, w->ln2_w, opt(cfg, w->ln2_b), cfg->norm_eps, sv.a2, sv.stats2, s));
   g = lin_fwd(d, sv.a2, C, w->w_fc, 4 * C, EPI_GELU);
   // inference keeps no GELU'(u): the epilogue then writes GELU(u) only
   g.out = saved ? sv.u : nullptr; g.out2 = sv.g; g.ldc = 4 * C; g.bias = opt(cfg, w->b_fc);
-  RUN("fc_gemm_gelu", launch_gemm(g, ty, nullptr, s));
+  if ((st = linear("fc_gemm_gelu", g, 4, sv.qa2T, sv.qWfcT))) return st;
   g = lin_fwd(d, sv.g, 4 * C, w->w_proj, C, EPI_STORE);
   g.out = y; g.ldc = C; g.bias = opt(cfg, w->b_proj); g.resid = sv.x1; g.ldr = C;
-  RUN("proj_gemm", launch_gemm(g, ty, nullptr, s));
+  if ((st = linear("proj_gemm", g, 6, sv.qgT, sv.qWprojT))) return st;
   return GPT_OK;
 }
 
@@ -484,29 +577,70 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   const int nblk = norm_bwd_blocks(N);
   const bool ln = kind == GPT_NORM_LAYERNORM;
 
+  // FP8 (cfg->fp8): each incoming gradient is quantized once (E5M2) into
+  // codes for its input-gradient GEMM and transposed codes for its weight-
+  // gradient GEMM, which runs right away (the code buffers serve the next
+  // layer); the weights' and activations' codes come from the forward.
+  // Gradient scale slots in b.f8sc: 0 dy, 1 du, 2 dx1, 3 dqkv.
+  const bool f8 = cfg->fp8 != 0;
+  auto fp8_grad = [&](const void* dY, int Out, int slot) -> int {
+    RUN("fp8_quant_g", launch_fp8_quantize_2d(N, Out, dY, FP8_E5M2, b.qg, b.qgT, fp8_np(N), b.f8sc + 4 * slot,
+                                              b.f8part, s));
+    return GPT_OK;
+  };
+  // dX[N][In] = q(dY) q(W): the forward's transposed weight codes [In][ld64(Out)]
+  auto fp8_dgrad = [&](const char* name, GemmDesc g, int Out, const uint8_t* qWT, int In, int gslot,
+                       int wslot) -> int {
+    g.A = b.qg; g.lda = Out; g.a_kmaj = false;
+    g.B = qWT; g.ldb = fp8_ld64(Out); g.b_kmaj = false;
+    g.M = N; g.N = In; g.K = Out;
+    g.f8_sa = b.f8sc + 4 * gslot; g.f8_sb = sv.f8sc + 4 * wslot;
+    RUN(name, launch_gemm_fp8(g, 2, nullptr, s));
+    return GPT_OK;
+  };
+  // dW[Out][In] (+)= q(dY)^T q(X): the gradient's and the activation's transposed codes
+  auto fp8_wg = [&](const char* name, int Out, const uint8_t* qxT, int In, float* dW, int gslot, int xslot) -> int {
+    GemmDesc g = fp8_wgrad(d, b.qgT, Out, qxT, In, dW, accumulate);
+    g.f8_sa = b.f8sc + 4 * gslot; g.f8_sb = sv.f8sc + 4 * xslot;
+    RUN(name, launch_gemm_fp8(g, 2, b.split, s));
+    return GPT_OK;
+  };
+
   // bf16: the input gradients through W_fc, W_o and W_qkv read transposed
   // copies (k contiguous on both sides of those GEMMs); W_proj's is read as
   // it lies (its wide tiles run as fast either way)
-  const bool wt = ty == GPT_DTYPE_BF16;
+  const bool wt = ty == GPT_DTYPE_BF16 && !f8;
   if (wt) {
     const TransposeDesc td[3] = {{w->w_fc, b.wt_fc, 4 * C, C}, {w->w_o, b.wt_o, C, C}, {w->w_qkv, b.wt_qkv, 3 * C, C}};
     RUN("weight_transpose", launch_transpose(td, 3, s));
   }
+  // weight gradients depend on nothing computed later: in bf16 they are
+  // gathered and run as one grouped launch at the end of the backward (one
+  // launch fills the machine where each alone would leave CUs idle)
+  GemmDesc wg[GEMM_GROUP_MAX];
+  int nwg = 0;
   // MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
   GemmDesc g = lin_dgrad(d, dy, C, w->w_proj, 4 * C, EPI_GELU_BWD);
   g.out = b.du; g.ldc = 4 * C; g.aux = sv.u; g.ldaux = 4 * C;
-  RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
-  // weight gradients depend on nothing computed later: they are gathered and
-  // run as one grouped launch at the end of the backward (one launch fills
-  // the machine where each alone would leave CUs idle)
-  GemmDesc wg[GEMM_GROUP_MAX];
-  int nwg = 0;
-  wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
+  if (f8) {
+    if ((st = fp8_grad(dy, C, 0))) return st;
+    if ((st = fp8_dgrad("proj_dgrad_gelu", g, C, sv.qWprojT, 4 * C, 0, 7))) return st;
+    if ((st = fp8_wg("proj_wgrad", C, sv.qgT, 4 * C, gr->w_proj, 0, 6))) return st;
+  } else {
+    RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
+    wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
+  }
   if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
   g = wt ? lin_dgrad_t(d, b.du, 4 * C, b.wt_fc, C, EPI_STORE) : lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
-  RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
-  wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
+  if (f8) {
+    if ((st = fp8_grad(b.du, 4 * C, 1))) return st;
+    if ((st = fp8_dgrad("fc_dgrad", g, 4 * C, sv.qWfcT, C, 1, 5))) return st;
+    if ((st = fp8_wg("fc_wgrad", 4 * C, sv.qa2T, C, gr->w_fc, 1, 4))) return st;
+  } else {
+    RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
+    wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
+  }
   if (cfg->bias) RUN("fc_bias", launch_colsum(ty, N, 4 * C, 4 * C, b.du, gr->b_fc, accumulate, b.colsum, s));
   // norm 2 backward + residual
   RUN("norm2_bwd", launch_norm_bwd(ty, kind, N, C, sv.x1, w->ln2_w, b.da, dy, cfg->norm_eps, b.dx1, b.colpart, ln, s));
@@ -517,8 +651,14 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   // attention output projection
   g = wt ? lin_dgrad_t(d, b.dx1, C, b.wt_o, C, EPI_STORE) : lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
   g.out = b.dO; g.ldc = C;
-  RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
-  wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
+  if (f8) {
+    if ((st = fp8_grad(b.dx1, C, 2))) return st;
+    if ((st = fp8_dgrad("out_dgrad", g, C, sv.qWoT, C, 2, 3))) return st;
+    if ((st = fp8_wg("out_wgrad", C, sv.qoT, C, gr->w_o, 2, 2))) return st;
+  } else {
+    RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
+    wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
+  }
   if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
   // attention
   const QkBwd qk{cfg->rope, cfg->qk_norm, N, sv.cs, sv.qkr};
@@ -541,8 +681,14 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   g = wt ? lin_dgrad_t(d, b.dqkv, 3 * C, b.wt_qkv, C, EPI_STORE)
          : lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
-  RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
-  wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);
+  if (f8) {
+    if ((st = fp8_grad(b.dqkv, 3 * C, 3))) return st;
+    if ((st = fp8_dgrad("qkv_dgrad", g, 3 * C, sv.qWqkvT, C, 3, 1))) return st;
+    if ((st = fp8_wg("qkv_wgrad", 3 * C, sv.qa1T, C, gr->w_qkv, 3, 0))) return st;
+  } else {
+    RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
+    wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);
+  }
   if (cfg->bias) RUN("qkv_bias", launch_colsum(ty, N, 3 * C, 3 * C, b.dqkv, gr->b_qkv, accumulate, b.colsum, s));
   // norm 1 backward + residual
   RUN("norm1_bwd", launch_norm_bwd(ty, kind, N, C, x, w->ln1_w, b.da, b.dx1, cfg->norm_eps, dx, b.colpart, ln, s));
@@ -550,7 +696,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln1_w, accumulate, s));
     if (cfg->bias) RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln1_b, accumulate, s));
   }
-  RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, split_need(d), s));
+  if (nwg) RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, split_need(d, cfg), s));
   return GPT_OK;
 }
 

@@ -115,6 +115,63 @@ __global__ __launch_bounds__(Q_THREADS) void quant_k(long n, const bf16* __restr
   }
 }
 
+// Codes of a bf16 matrix x [R][Cc] (Cc a multiple of 16) with one scale, in
+// 64 x 64 tiles: q [R][Cc] (when given) by 8-byte row stores, and the
+// transpose qT [Cc][ldT] (when given) through a 4 KB LDS tile, by 16-byte
+// row stores; qT columns R .. ldT - 1 (rows of x beyond R) receive zeros.
+// Thread t quantizes the 8-element vectors (row t / 8 + 32 v, columns
+// 8 (t % 8) ..) of the tile, v = 0, 1.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant2d_k(int R, int Cc, const bf16* __restrict__ x,
+                                                 const float* __restrict__ scal, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ qT, long ldT) {
+  __shared__ uint32_t tile[64][17];  // 64 rows x 64 codes, padded row
+  const float s = scal[0];
+  const float mx = FMT == FP8_E5M2 ? 57344.0f : 448.0f;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int rr = t / 8 + 32 * v, cc = 8 * (t % 8);
+    const int r = r0 + rr, c = c0 + cc;
+    uint32_t lo = 0, hi = 0;
+    if (r < R && c < Cc) {
+      float f[8];
+      Vec8<bf16>::load(x + (long)r * Cc + c, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(f[i] * s, -mx), mx);
+      int a = cvt_pair<FMT, false>(f[0], f[1], 0);
+      a = cvt_pair<FMT, true>(f[2], f[3], a);
+      int b = cvt_pair<FMT, false>(f[4], f[5], 0);
+      b = cvt_pair<FMT, true>(f[6], f[7], b);
+      lo = (uint32_t)a;
+      hi = (uint32_t)b;
+      if (q) *reinterpret_cast<uint2*>(q + (long)r * Cc + c) = make_uint2(lo, hi);
+    }
+    tile[rr][cc / 4] = lo;
+    tile[rr][cc / 4 + 1] = hi;
+  }
+  if (!qT) return;
+  __syncthreads();
+  // output row c0 + j of qT: bytes r0 + 16 g .. + 15 (source rows) of
+  // source column j; thread t: j = t / 4, g = t % 4
+  const int j = t / 4, g = t % 4;
+  if (c0 + j >= Cc) return;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t code = (tile[16 * g + 4 * k + e][j / 4] >> (8 * (j % 4))) & 0xffu;
+      word |= code << (8 * e);
+    }
+    w[k] = word;
+  }
+  if (r0 + 16 * g < ldT)
+    *reinterpret_cast<uint4*>(qT + (long)(c0 + j) * ldT + r0 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ------------------------------------------------------------ GEMM
 constexpr int F_BM = 256, F_BN = 256, F_NT = 512, F_BK = 128;  // BK in bytes (elements)
 constexpr int F_TM = 4, F_TN = 2;                              // 32 x 32 tiles per wave (128 x 64)
@@ -266,5 +323,24 @@ hipError_t launch_fp8_gemm(int M, int N, int K, const void* A, long lda, int fa,
   else if (fa == FP8_E4M3 && fb == FP8_E5M2) FG(FP8_E4M3, FP8_E5M2);
   else FG(FP8_E5M2, FP8_E5M2);
 #undef FG
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_2d(int R, int Cc, const void* x, int fmt, void* q, void* qT, long ldT, float* scal,
+                                  float* part, hipStream_t s) {
+  if (R <= 0 || Cc <= 0 || Cc % 16 || (qT && (ldT < R || ldT % 64))) return hipErrorInvalidValue;
+  const long n = (long)R * Cc;
+  const long nb = fp8_amax_parts(n);
+  hipLaunchKernelGGL(amax_k, dim3((unsigned)nb), dim3(Q_THREADS), 0, s, n, (const bf16*)x, part);
+  hipLaunchKernelGGL(amax_finish_k, dim3(1), dim3(Q_THREADS), 0, s, (int)nb, (const float*)part, fmt, scal);
+  // with the transpose, the tiles cover the padded rows R .. ldT - 1 too (zeros)
+  const int rows = qT ? (int)ldT : R;
+  dim3 grid(cdiv(Cc, 64), cdiv(rows, 64));
+  if (fmt == FP8_E5M2)
+    hipLaunchKernelGGL(quant2d_k<FP8_E5M2>, grid, dim3(256), 0, s, R, Cc, (const bf16*)x, (const float*)scal,
+                       (uint8_t*)q, (uint8_t*)qT, ldT);
+  else
+    hipLaunchKernelGGL(quant2d_k<FP8_E4M3>, grid, dim3(256), 0, s, R, Cc, (const bf16*)x, (const float*)scal,
+                       (uint8_t*)q, (uint8_t*)qT, ldT);
   return hipGetLastError();
 }

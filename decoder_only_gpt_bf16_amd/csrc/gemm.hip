@@ -282,6 +282,40 @@ struct StageKm {
 template <bool KMAJ, int R, int NT>
 using Stage = typename std::conditional<KMAJ, StageKm<R, NT>, StageKc<R, NT>>::type;
 
+// FP8 operand (byte codes, k contiguous): R rows x 128 k of a k tile, LDS
+// [row][8 units] with the same swizzle as StageKc (128-byte rows either way).
+typedef int v8i __attribute__((ext_vector_type(8)));
+template <int R, int NT>
+struct Stage8 {
+  static constexpr int NL = (R * 8 + NT - 1) / NT;
+  static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                int k0, int kend) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if ((R * 8) % NT != 0 && NT / 64 * i + w >= R * 8 / 64) break;
+      const int P = (NT / 64 * i + w) * 64 + lane;
+      const int row = P >> 3;
+      const int u = (P & 7) ^ swz128(row);
+      const int gr = r0 + row, kk = k0 + 16 * u;
+      const uint32_t off = (kk + 16 <= kend && gr < rmax) ? (uint32_t)((long)gr * ld + kk) : OOB;
+      load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
+    }
+  }
+  // 32 bytes of tile row `row` for the 64-wide k-step ks (0, 1) and lane
+  // half hf: units 4 ks + hf and 4 ks + 2 + hf.  Which k a byte stands for
+  // only has to agree between the two operands: the instruction pairs byte
+  // j of lane (row, half) of one with byte j of the same half of the other.
+  static __device__ __forceinline__ v8i frag(const uint4* lds, int row, int ks, int hf) {
+    const uint4 a = lds[row * 8 + ((4 * ks + hf) ^ swz128(row))];
+    const uint4 b = lds[row * 8 + ((4 * ks + 2 + hf) ^ swz128(row))];
+    v8i v;
+    v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
+    v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
+    return v;
+  }
+};
+
 // Explicit waits: the compiler's own waits know nothing of the direct
 // global -> LDS copies, and a plain __syncthreads would also drain them.
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -305,7 +339,10 @@ struct Frags {
 // One output tile (tm, tn) over k in [kbeg, kend).  part == nullptr: the
 // epilogue of EPI; else the raw fp32 accumulators go to part as a dense
 // BM x BN tile (a partial sum for a later fixed-order reduction).
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+// F8 != 0: FP8 operands (F8 = 1: A and B E4M3; 2: A E5M2, B E4M3), k tiles
+// of 128 bytes, one v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales)
+// per 64 k; the accumulators are dequantized before the epilogue.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM, int F8 = 0>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, int kbeg, int kend,
                                           float* __restrict__ part) {
   constexpr int NT = NW * 64;
@@ -367,7 +404,48 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   // the explicit pipeline keeps two fragment sets live; wide 8-wave tiles
   // (64 x 160 per wave) cannot afford them and use the compiler's schedule
   constexpr bool PIPE = NW == 8 && TM * TN <= 8;
-  if constexpr (PIPE) {
+  if constexpr (F8 != 0) {
+    static_assert(!A_KMAJ && !B_KMAJ, "FP8 operands are k-contiguous");
+    constexpr int FA = F8 == 2 ? 1 : 0, FB = 0;  // instruction format codes: 0 E4M3, 1 E5M2
+    (void)F;
+    const int nk8 = kend > kbeg ? (kend - kbeg + 127) / 128 : 0;
+    auto issue8 = [&](int t) {
+      uint4* st = lds + (t & 1) * STAGE_UNITS;
+      const int k0 = kbeg + t * 128;
+      Stage8<BM, NT>::direct(st, ra, p.lda, m0, p.M, k0, kend);
+      Stage8<BN, NT>::direct(st + SA_UNITS, rb, p.ldb, n0, p.N, k0, kend);
+    };
+    if (nk8 > 0) issue8(0);
+    wait_loads();
+    __syncthreads();
+    for (int t = 0; t < nk8; ++t) {
+      if (t + 1 < nk8) issue8(t + 1);
+      const uint4* As = lds + (t & 1) * STAGE_UNITS;
+      const uint4* Bs = As + SA_UNITS;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i a[TM], b[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = Stage8<BM, NT>::frag(As, wm + 32 * i + lrow, ks, lhalf);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = Stage8<BN, NT>::frag(Bs, wn + 32 * j + lrow, ks, lhalf);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[j][i], FB, FA, 0, 127, 0, 127);
+      }
+      wait_loads();
+      __syncthreads();
+    }
+    const float inv = p.f8_sa[2] * p.f8_sb[2];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] *= inv;
+  } else if constexpr (PIPE) {
     if (nk > 0) {
       issue(0);
       wait_loads();
@@ -659,12 +737,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   }
 }
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM, int F8 = 0>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_mfma(GemmParams p) {
   int tm, tn;
   tile_coords(p, blockIdx.x, gridDim.x, tm, tn);
   const int kbeg = blockIdx.z * p.k_split;
-  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, tm, tn, kbeg, min(p.K, kbeg + p.k_split), nullptr);
+  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM, F8>(p, tm, tn, kbeg, min(p.K, kbeg + p.k_split), nullptr);
 }
 
 // Several independent problems of one kind in a single launch: blocks
@@ -869,13 +947,13 @@ Plan plan_mfma(const GemmDesc& d) {
 // the fused RoPE / QK-norm epilogue, whose waves each hold one head); in the
 // LM-head statistics a wave's 64 columns make one (max, sum exp) partial.
 // 128 x 128 tiles run 4 waves of 64 x 64.
-template <bool AK, bool BKm, int EPI, int BMv, int BNv>
+template <bool AK, bool BKm, int EPI, int BMv, int BNv, int F8 = 0>
 hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
   if constexpr (BMv == 256)
-    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 8, 2, F8>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, BMv, BNv, 4, 2, F8>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -883,16 +961,16 @@ hipError_t go_mfma(const GemmParams& p, int splits, hipStream_t s) {
 // whole rounds and 256 x 256 would not; 256 x 160 (N a multiple of 160, e.g.
 // 1280 = 8 x 160 with M = 8192: exactly one tile per CU) as 8 waves of
 // 32 x 160, two per SIMD.
-template <bool AK, bool BKm, int EPI>
+template <bool AK, bool BKm, int EPI, int F8 = 0>
 hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
-  if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256>(p, pl.splits, s);
+  if (pl.BMv == 256 && pl.BNv == 256) return go_mfma<AK, BKm, EPI, 256, 256, F8>(p, pl.splits, s);
   if (pl.BNv == 320) {
     // 8 waves of 64 x 160
     if constexpr (EPI == EPI_XENT_STATS || EPI == EPI_QKNORM || EPI == EPI_F32) {
       return hipErrorInvalidValue;
     } else {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
-      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 320, 8, 4>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 320, 8, 4, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
     }
   }
@@ -901,11 +979,11 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
       return hipErrorInvalidValue;
     } else {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
-      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 160, 8, 8>), grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 160, 8, 8, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
     }
   }
-  return go_mfma<AK, BKm, EPI, 128, 128>(p, pl.splits, s);
+  return go_mfma<AK, BKm, EPI, 128, 128, F8>(p, pl.splits, s);
 }
 
 template <typename T, bool AK, bool BKm, int EPI>
@@ -926,6 +1004,7 @@ GemmParams make_params(const GemmDesc& d) {
   p.part_off = d.part_off; p.ztgt = d.ztgt; p.lse = d.lse; p.scale = d.scale; p.roww = d.roww;
   p.qk_cs = d.qk_cs; p.qk_rstd = d.qk_rstd; p.qk_T = d.qk_T; p.qk_rope = d.qk_rope; p.qk_norm = d.qk_norm;
   p.qk_eps = d.qk_eps;
+  p.f8_sa = d.f8_sa; p.f8_sb = d.f8_sb;
   return p;
 }
 
@@ -1086,6 +1165,66 @@ hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s) {
       break;
   }
   return hipErrorInvalidValue;
+}
+
+// FP8 GEMMs: the MFMA path's tile plan with 128-element k tiles for split-K.
+static Plan plan_fp8(const GemmDesc& d) {
+  Plan pl = plan_mfma(d);
+  pl.k_split = cdiv(cdiv(d.K, pl.splits), 128) * 128;
+  pl.splits = cdiv(d.K, pl.k_split);
+  return pl;
+}
+
+size_t gemm_fp8_split_scratch_bytes(const GemmDesc& d) {
+  if (d.epi != EPI_F32) return 0;
+  const Plan pl = plan_fp8(d);
+  return pl.splits > 1 ? align256((size_t)pl.splits * d.M * d.N * sizeof(float)) : 0;
+}
+
+hipError_t launch_gemm_fp8(const GemmDesc& d, int mode, void* ws, hipStream_t s) {
+  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  if (d.a_kmaj || d.b_kmaj || d.K <= 0 || d.K % 16 || d.lda % 16 || d.ldb % 16 || !d.f8_sa || !d.f8_sb)
+    return hipErrorInvalidValue;
+  const long ab = (long)(d.M - 1) * d.lda + d.K, bb = (long)(d.N - 1) * d.ldb + d.K;
+  if (ab >= (1L << 31) || bb >= (1L << 31)) return hipErrorInvalidValue;
+  GemmParams p = make_params(d);
+  const Plan pl = plan_fp8(d);
+  p.tiles_m = cdiv(d.M, pl.BMv);
+  p.tiles_n = cdiv(d.N, pl.BNv);
+  p.k_split = pl.k_split;
+  p.a_bytes = (uint32_t)ab;
+  p.b_bytes = (uint32_t)bb;
+  const bool split = pl.splits > 1;
+  if (split) {
+    p.out = ws; p.ldc = d.N; p.accumulate = 0; p.split_stride = (long)d.M * d.N;
+  }
+  hipError_t e = hipErrorInvalidValue;
+  if (mode == 1) {
+    switch (d.epi) {
+      case EPI_STORE: e = go_mfma_tiles<false, false, EPI_STORE, 1>(p, pl, s); break;
+      case EPI_GELU: e = go_mfma_tiles<false, false, EPI_GELU, 1>(p, pl, s); break;
+      case EPI_QKNORM:
+        if (d.N % 384 == 0) e = go_mfma<false, false, EPI_QKNORM, 256, 256, 1>(p, pl.splits, s);
+        break;
+      default: break;
+    }
+  } else if (mode == 2) {
+    switch (d.epi) {
+      case EPI_STORE: e = go_mfma_tiles<false, false, EPI_STORE, 2>(p, pl, s); break;
+      case EPI_GELU_BWD: e = go_mfma_tiles<false, false, EPI_GELU_BWD, 2>(p, pl, s); break;
+      case EPI_F32: e = go_mfma_tiles<false, false, EPI_F32, 2>(p, pl, s); break;
+      default: break;
+    }
+  }
+  if (e != hipSuccess) return e;
+  if (split) {
+    const long total = (long)d.M * d.N;
+    int blocks = (int)std::min<long>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, s, (const float*)ws, pl.splits, (long)d.M * d.N,
+                       d.M, d.N, (float*)d.out, d.ldc, d.accumulate);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // Stream-K plan of a weight-gradient group: 256 x 256 tiles over

@@ -58,6 +58,9 @@ struct GemmParams {
   float* qk_rstd;
   int qk_T, qk_rope, qk_norm;
   float qk_eps;
+  // FP8 operands: quantizer scale arrays of A and B (element 2 = 1 / scale)
+  const float* f8_sa;
+  const float* f8_sb;
 };
 
 struct GemmDesc {
@@ -74,6 +77,7 @@ struct GemmDesc {
   const int32_t* tgt; int col_offset; float2* part; int part_ld; int part_off;
   float* ztgt; const float* lse; float scale; const float* roww;
   const float2* qk_cs; float* qk_rstd; int qk_T, qk_rope, qk_norm; float qk_eps;
+  const float* f8_sa; const float* f8_sb;  // launch_gemm_fp8: operands' scale arrays
 };
 
 // Bytes of split-K scratch launch_gemm may use for this problem (0 if none).
@@ -82,6 +86,11 @@ size_t gemm_split_scratch_bytes(const GemmDesc& d, int dtype);
 int xent_part_cols();
 // Launch; `ws` provides split-K scratch of gemm_split_scratch_bytes().
 hipError_t launch_gemm(const GemmDesc& d, int dtype, void* ws, hipStream_t s);
+// The same GEMM with FP8 operands (byte codes, k contiguous on both sides,
+// K, lda and ldb multiples of 16), dequantized by f8_sa[2] * f8_sb[2] before
+// the epilogue.  mode 1: A and B E4M3; mode 2: A E5M2, B E4M3.
+hipError_t launch_gemm_fp8(const GemmDesc& d, int mode, void* ws, hipStream_t s);
+size_t gemm_fp8_split_scratch_bytes(const GemmDesc& d);
 // Up to GEMM_GROUP_MAX independent fp32-output (EPI_F32) problems with both
 // operands k-major and one K (the weight gradients of a block) as one
 // stream-K launch plus a fixed-order fixup of the tiles split between
@@ -219,6 +228,11 @@ constexpr int FP8_E4M3 = 0, FP8_E5M2 = 1;
 long fp8_amax_parts(long n);
 // scal (device float[3]) <- scale, amax, 1 / scale; q <- codes; part: fp8_amax_parts(n) floats
 hipError_t launch_fp8_quantize(long n, const void* x, int fmt, void* q, float* scal, float* part, hipStream_t s);
+// A bf16 matrix x [R][Cc] (Cc a multiple of 16) quantized with one scale:
+// scal as above; q [R][Cc] codes (or NULL) and qT [Cc][ldT] transposed codes
+// (or NULL; ldT >= R a multiple of 64, columns R .. ldT - 1 zero).
+hipError_t launch_fp8_quantize_2d(int R, int Cc, const void* x, int fmt, void* q, void* qT, long ldT, float* scal,
+                                  float* part, hipStream_t s);
 // out (bf16, ldc) = A B^T * scal_a[2] * scal_b[2]; A [M][lda], B [N][ldb] codes, k contiguous
 hipError_t launch_fp8_gemm(int M, int N, int K, const void* A, long lda, int fa, const float* scal_a, const void* B,
                            long ldb, int fb, const float* scal_b, void* out, long ldc, hipStream_t s);

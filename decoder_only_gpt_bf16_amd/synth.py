@@ -56,6 +56,7 @@ class GPTConfig:
     eps: float = 1e-5
     dtype: str = "bf16"          # storage type: "bf16" or "fp32"
     window: int = 0              # sliding attention window (keys i-W+1..i); 0: full causal
+    fp8: bool = False            # the block's Linear layers as FP8 GEMMs
     tied: bool = True            # lm_head weight is wte
     vocab_real: Optional[int] = None  # ids are drawn below this (padded vocab)
 
@@ -264,7 +265,7 @@ def oracle_cfg(cfg: GPTConfig) -> dict:
     return dict(n_layer=cfg.n_layer, n_head=cfg.n_head, n_embd=cfg.n_embd,
                 vocab_size=cfg.vocab_size, norm=cfg.norm, bias=cfg.bias,
                 rope=cfg.rope, qk_norm=cfg.qk_norm, rope_base=cfg.rope_base,
-                eps=cfg.eps, window=cfg.window)
+                eps=cfg.eps, window=cfg.window, fp8=cfg.fp8)
 
 
 def make_adamw_inputs(shapes, seed: int = 0, g_std: float = 1e-2):

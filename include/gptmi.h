@@ -80,6 +80,14 @@ typedef struct gpt_config {
                           sliding windows of the "SSSL" layer pattern,
                           [nanochat] 6.2; per-layer windows are per-call
                           configs).  W >= T is the full causal mask.      */
+  int32_t fp8;         /* 1: the four Linear layers of gpt_block_fwd/bwd run
+                          as FP8 GEMMs ([nanochat] 6.2, FP8 paragraph):
+                          activations and weights E4M3, gradients E5M2, each
+                          quantized from its bf16 value with a dynamic
+                          per-tensor scale (fmt_max / amax), fp32
+                          accumulation; both backward matmuls in FP8 too.
+                          bf16 storage and n_embd % 16 == 0 required.  0:
+                          bf16 GEMMs.                                      */
 } gpt_config;
 
 /* Block parameters (device pointers, storage dtype).  Absent ones are NULL:

@@ -68,7 +68,11 @@ def row_errors(a, b):
     return row, elem
 
 
-def assert_rel(name, got, ref, tol, report=None):
+def assert_rel(name, got, ref, tol, report=None, row_tol=None, elem_tol=None):
+    """Global, per-row and per-element bounds (row_tol, elem_tol default to
+    the bf16-derived ROW_TOL, ELEM_TOL)."""
+    row_tol = ROW_TOL if row_tol is None else row_tol
+    elem_tol = ELEM_TOL if elem_tol is None else elem_tol
     g = np.asarray(got, dtype=np.float64)
     r = rel(g, ref)
     if report is not None:
@@ -81,8 +85,8 @@ def assert_rel(name, got, ref, tol, report=None):
     assert r <= tol, f"{name}: rel err {r:.3e} > {tol:.1e}"
     if row is not None:
         if np.asarray(ref).ndim >= 2:
-            assert row <= ROW_TOL, f"{name}: a row's rel err {row:.3e} > {ROW_TOL:.2e}"
-        assert elem <= ELEM_TOL, f"{name}: an element's err {elem:.3e} of its row scale > {ELEM_TOL:.2e}"
+            assert row <= row_tol, f"{name}: a row's rel err {row:.3e} > {row_tol:.2e}"
+        assert elem <= elem_tol, f"{name}: an element's err {elem:.3e} of its row scale > {elem_tol:.2e}"
     return r
 
 

@@ -14,13 +14,25 @@ import torch
 import oracle as O
 from decoder_only_gpt_bf16_amd import binding as B
 from decoder_only_gpt_bf16_amd import synth
-from decoder_only_gpt_bf16_amd.model import to_f64
+from decoder_only_gpt_bf16_amd.model import BlockRunner, to_f64
 from tests._parity import assert_rel, print_case
 
 pytestmark = pytest.mark.gpu
 
 FMT = {"e4m3": B.FP8_E4M3, "e5m2": B.FP8_E5M2}
 REL_FP8_GEMM = 1e-2
+# The block with FP8 Linear layers against the oracle's FP8 block.  Both
+# quantize nearly equal bf16 inputs, with nearly equal per-tensor scales;
+# where the two inputs fall on either side of a rounding boundary of the
+# format the codes differ by one step of it, so the two results differ at
+# the scale of FP8 rounding itself rather than of bf16's.  The gradient
+# operand is E5M2 (2 mantissa bits, relative half-step 2^-3), which bounds
+# the per-tensor difference: REL_FP8 = 2^-3 (worst measured 8.4%, dW_qkv).
+# Rows and single elements average fewer such disagreements, as in the bf16
+# bounds: 2^-1 per row (worst measured 0.22) and 2 per element of its row's
+# scale (worst measured 1.25, a LayerNorm gain gradient).  A wrong scale,
+# operand or layout misses these by an order of magnitude or more.
+REL_FP8, REL_FP8_ROW, REL_FP8_ELEM = 2.0 ** -3, 2.0 ** -1, 2.0
 
 
 def _bf16(a):
@@ -108,3 +120,31 @@ def test_fp8_linear_end_to_end():
     assert_rel("C(sampled rows)", got, ref, REL_FP8_GEMM)
     full = x[rows] @ w.T
     assert np.linalg.norm(got - full) / np.linalg.norm(full) < 0.1
+
+
+# ---- the block with FP8 Linear layers (gpt_config.fp8) against the oracle's
+# FP8 block ----
+FP8_BLOCK = [("d20_block", dict(B=2, T=200)), ("gpt2_block", dict(B=2, T=200)), ("d20_block", dict(B=1, T=77)),
+             ("d20_block", dict()), ("gpt2_block", dict())]
+
+
+@pytest.mark.parametrize("name,sz", FP8_BLOCK, ids=[f"{n}-{s.get('B', 'full')}-{s.get('T', 'full')}" for n, s in FP8_BLOCK])
+def test_fp8_block_parity(name, sz):
+    w = synth.scaled(synth.BY_NAME[name], fp8=True, **sz)
+    print_case("fp8-block", name, w.B, w.T)
+    x, dy, p = synth.make_block_inputs(w)
+    r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
+    r.step()
+    torch.cuda.synchronize()
+    cfg = synth.oracle_cfg(w.cfg)
+    y_ref, cache = O.block_fwd(cfg, x, p)
+    dx_ref, g_ref = O.block_bwd(cfg, dy, cache, p)
+    rep = {}
+    y = to_f64(r.y).reshape(x.shape)
+    kw = dict(row_tol=REL_FP8_ROW, elem_tol=REL_FP8_ELEM)
+    assert_rel("y-x", y - x, y_ref - x, REL_FP8, rep, **kw)
+    assert_rel("dx", to_f64(r.dx).reshape(x.shape), dx_ref, REL_FP8, rep, **kw)
+    for k, v in g_ref.items():
+        if v is not None:
+            assert_rel("d" + k, to_f64(r.g[k]), v, REL_FP8, rep, **kw)
+    print(name, w.B, w.T, {k: f"{v:.2e}" for k, v in rep.items()})
