@@ -185,18 +185,22 @@ Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   return s;
 }
 
-// FP8 forward temporaries: codes of the current Linear's activation and
-// weight, amax partials
+// FP8 forward temporaries: codes of the current Linear's activation, of the
+// four weights (qkv, o, fc, proj), amax partials
 struct Fp8FwdWs {
-  uint8_t *qx, *qw;
+  uint8_t* qx;
+  uint8_t* qw[4];
   float* part;
 };
 Fp8FwdWs fp8_fwd_layout(const Dims& d, Arena& a) {
   Fp8FwdWs f{};
   const size_t N = d.N, C = d.C;
   f.qx = a.take_n<uint8_t>(N * 4 * C);
-  f.qw = a.take_n<uint8_t>(4 * C * C);
-  f.part = a.take_n<float>(std::max(fp8_amax_parts((long)N * 4 * C), fp8_amax_parts(4L * C * C)));
+  f.qw[0] = a.take_n<uint8_t>(3 * C * C);
+  f.qw[1] = a.take_n<uint8_t>(C * C);
+  f.qw[2] = a.take_n<uint8_t>(4 * C * C);
+  f.qw[3] = a.take_n<uint8_t>(4 * C * C);
+  f.part = a.take_n<float>(fp8_q2d_parts(4));
   return f;
 }
 
@@ -306,7 +310,7 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   if (cfg->fp8) {
     w.qg = a.take_n<uint8_t>(N * 4 * C);
     w.qgT = a.take_n<uint8_t>(4 * C * fp8_np(N));
-    w.f8part = a.take_n<float>(fp8_amax_parts((long)N * 4 * C));
+    w.f8part = a.take_n<float>(fp8_q2d_parts(1));
     w.f8sc = a.take_n<float>(16);
   }
   return w;
@@ -496,24 +500,32 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   Arena fa = saved ? Arena(ws) : sa;  // FP8 temporaries follow the intermediates
   const Fp8FwdWs fw = cfg->fp8 ? fp8_fwd_layout(d, fa) : Fp8FwdWs{};
 
-  // One Linear layer: the bf16 GEMM, or with cfg->fp8 the activation and the
-  // weight quantized to E4M3 (their transposed codes kept in `saved` for the
+  // FP8: the four weights quantized to E4M3 in one pass (codes for the
+  // forward GEMMs, transposed codes kept in `saved` for the backward's)
+  if (cfg->fp8) {
+    const Fp8Q2d qw[4] = {
+        {w->w_qkv, fw.qw[0], saved ? sv.qWqkvT : nullptr, fp8_ld64(3 * C), 3 * C, C, sv.f8sc + 4 * 1},
+        {w->w_o, fw.qw[1], saved ? sv.qWoT : nullptr, fp8_ld64(C), C, C, sv.f8sc + 4 * 3},
+        {w->w_fc, fw.qw[2], saved ? sv.qWfcT : nullptr, fp8_ld64(4 * C), 4 * C, C, sv.f8sc + 4 * 5},
+        {w->w_proj, fw.qw[3], saved ? sv.qWprojT : nullptr, fp8_ld64(C), C, 4 * C, sv.f8sc + 4 * 7}};
+    RUN("fp8_quant_w", launch_fp8_quantize_2d(qw, 4, FP8_E4M3, fw.part, s));
+  }
+  // One Linear layer: the bf16 GEMM, or with cfg->fp8 the activation
+  // quantized to E4M3 (its transposed codes kept in `saved` for the
   // backward) and the FP8 GEMM with the same epilogue.  slot: the
-  // activation's scale slot in sv.f8sc, the weight's is slot + 1.
-  auto linear = [&](const char* name, GemmDesc g, int slot, uint8_t* qxT, uint8_t* qwT) -> int {
+  // activation's scale slot in sv.f8sc, the weight's is slot + 1; wi: the
+  // weight's codes in fw.qw.
+  auto linear = [&](const char* name, GemmDesc g, int slot, uint8_t* qxT, int wi) -> int {
     if (!cfg->fp8) {
       RUN(name, launch_gemm(g, ty, nullptr, s));
       return GPT_OK;
     }
-    const int In = g.K, Out = g.N;
+    const int In = g.K;
     float* sx = sv.f8sc + 4 * slot;
-    float* sw = sv.f8sc + 4 * (slot + 1);
-    RUN("fp8_quant_w", launch_fp8_quantize_2d(Out, In, g.B, FP8_E4M3, fw.qw, saved ? qwT : nullptr,
-                                              fp8_ld64(Out), sw, fw.part, s));
-    RUN("fp8_quant_x", launch_fp8_quantize_2d(d.N, In, g.A, FP8_E4M3, fw.qx, saved ? qxT : nullptr, fp8_np(d.N),
-                                              sx, fw.part, s));
-    g.A = fw.qx; g.lda = In; g.B = fw.qw; g.ldb = In;
-    g.f8_sa = sx; g.f8_sb = sw;
+    const Fp8Q2d qx = {g.A, fw.qx, saved ? qxT : nullptr, fp8_np(d.N), d.N, In, sx};
+    RUN("fp8_quant_x", launch_fp8_quantize_2d(&qx, 1, FP8_E4M3, fw.part, s));
+    g.A = fw.qx; g.lda = In; g.B = fw.qw[wi]; g.ldb = In;
+    g.f8_sa = sx; g.f8_sb = sv.f8sc + 4 * (slot + 1);
     RUN(name, launch_gemm_fp8(g, 1, nullptr, s));
     return GPT_OK;
   };
@@ -530,21 +542,21 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
     g.qk_cs = cs; g.qk_rstd = sv.qkr; g.qk_T = T; g.qk_rope = cfg->rope; g.qk_norm = cfg->qk_norm;
     g.qk_eps = cfg->norm_eps;
   }
-  if ((st = linear("qkv_gemm", g, 0, sv.qa1T, sv.qWqkvT))) return st;
+  if ((st = linear("qkv_gemm", g, 0, sv.qa1T, 0))) return st;
   if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
   RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, cfg->attn_window, sv.qkv, sv.o, sv.lse, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
   g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
-  if ((st = linear("out_gemm", g, 2, sv.qoT, sv.qWoT))) return st;
+  if ((st = linear("out_gemm", g, 2, sv.qoT, 1))) return st;
   RUN("norm2_fwd", launch_norm_fwd(ty, kind, d.N, C, sv.x1, w->ln2_w, opt(cfg, w->ln2_b), cfg->norm_eps, sv.a2, sv.stats2, s));
   g = lin_fwd(d, sv.a2, C, w->w_fc, 4 * C, EPI_GELU);
   // inference keeps no GELU'(u): the epilogue then writes GELU(u) only
   g.out = saved ? sv.u : nullptr; g.out2 = sv.g; g.ldc = 4 * C; g.bias = opt(cfg, w->b_fc);
-  if ((st = linear("fc_gemm_gelu", g, 4, sv.qa2T, sv.qWfcT))) return st;
+  if ((st = linear("fc_gemm_gelu", g, 4, sv.qa2T, 2))) return st;
   g = lin_fwd(d, sv.g, 4 * C, w->w_proj, C, EPI_STORE);
   g.out = y; g.ldc = C; g.bias = opt(cfg, w->b_proj); g.resid = sv.x1; g.ldr = C;
-  if ((st = linear("proj_gemm", g, 6, sv.qgT, sv.qWprojT))) return st;
+  if ((st = linear("proj_gemm", g, 6, sv.qgT, 3))) return st;
   return GPT_OK;
 }
 
@@ -584,8 +596,8 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   // Gradient scale slots in b.f8sc: 0 dy, 1 du, 2 dx1, 3 dqkv.
   const bool f8 = cfg->fp8 != 0;
   auto fp8_grad = [&](const void* dY, int Out, int slot) -> int {
-    RUN("fp8_quant_g", launch_fp8_quantize_2d(N, Out, dY, FP8_E5M2, b.qg, b.qgT, fp8_np(N), b.f8sc + 4 * slot,
-                                              b.f8part, s));
+    const Fp8Q2d qg = {dY, b.qg, b.qgT, fp8_np(N), N, Out, b.f8sc + 4 * slot};
+    RUN("fp8_quant_g", launch_fp8_quantize_2d(&qg, 1, FP8_E5M2, b.f8part, s));
     return GPT_OK;
   };
   // dX[N][In] = q(dY) q(W): the forward's transposed weight codes [In][ld64(Out)]

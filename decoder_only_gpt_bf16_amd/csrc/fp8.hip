@@ -21,6 +21,17 @@
 
 namespace {
 
+struct Q2dJobs {
+  const bf16* x[Q2D_MAX];
+  uint8_t* q[Q2D_MAX];
+  uint8_t* qT[Q2D_MAX];
+  long ldT[Q2D_MAX];
+  int R[Q2D_MAX], Cc[Q2D_MAX], tiles_c[Q2D_MAX];
+  int start[Q2D_MAX + 1];
+  float* scal[Q2D_MAX];
+  int n;
+};
+
 constexpr int Q_THREADS = 256;
 constexpr int Q_CHUNK = 4096;  // elements per block: 16 per thread
 
@@ -115,21 +126,75 @@ __global__ __launch_bounds__(Q_THREADS) void quant_k(long n, const bf16* __restr
   }
 }
 
-// Codes of a bf16 matrix x [R][Cc] (Cc a multiple of 16) with one scale, in
-// 64 x 64 tiles: q [R][Cc] (when given) by 8-byte row stores, and the
-// transpose qT [Cc][ldT] (when given) through a 4 KB LDS tile, by 16-byte
-// row stores; qT columns R .. ldT - 1 (rows of x beyond R) receive zeros.
-// Thread t quantizes the 8-element vectors (row t / 8 + 32 v, columns
-// 8 (t % 8) ..) of the tile, v = 0, 1.
+// Codes of up to Q2D_MAX bf16 matrices x_j [R_j][Cc_j] (Cc_j a multiple of
+// 16), one per-tensor scale each, of one format.  Two launches:
+//   amax_parts_k: AMAX_PARTS blocks per matrix, each the max |x| over a
+//     grid-stride share of its 8-element vectors (8 loads in flight);
+//   quant2d_k: 64 x 64 tiles; every block first reduces its matrix's
+//     AMAX_PARTS partials (4 KB) into amax and scale = fmt_max / amax (1 when
+//     amax is 0), the first block of a matrix also stores (scale, amax,
+//     1 / scale); then q [R][Cc] codes (when given) by 8-byte row stores and
+//     the transpose qT [Cc][ldT] (when given) through a 4 KB LDS tile by
+//     16-byte row stores, qT columns R .. ldT - 1 zero.
+constexpr int AMAX_PARTS = 1024;
+
+__global__ __launch_bounds__(256) void amax_parts_k(Q2dJobs J, float* __restrict__ part) {
+  const int j = blockIdx.x / AMAX_PARTS, b = blockIdx.x % AMAX_PARTS;
+  const long nv = (long)J.R[j] * J.Cc[j] / 8;
+  const bf16* x = J.x[j];
+  float m = 0.0f;
+  constexpr long STRIDE = 256L * AMAX_PARTS;
+  for (long v0 = (long)b * 256 + threadIdx.x; v0 < nv; v0 += 8 * STRIDE) {
+    uint4 f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const long v = v0 + u * STRIDE;
+      f[u] = v < nv ? *reinterpret_cast<const uint4*>(x + 8 * v) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t w4[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w4[e] << 16)), fabsf(__uint_as_float(w4[e] & 0xffff0000u))));
+    }
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 template <int FMT>
-__global__ __launch_bounds__(256) void quant2d_k(int R, int Cc, const bf16* __restrict__ x,
-                                                 const float* __restrict__ scal, uint8_t* __restrict__ q,
-                                                 uint8_t* __restrict__ qT, long ldT) {
+__global__ __launch_bounds__(256) void quant2d_k(Q2dJobs J, const float* __restrict__ part) {
   __shared__ uint32_t tile[64][17];  // 64 rows x 64 codes, padded row
-  const float s = scal[0];
-  const float mx = FMT == FP8_E5M2 ? 57344.0f : 448.0f;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  __shared__ float red[4];
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < Q2D_MAX; ++i)
+    if (i < J.n && (int)blockIdx.x >= J.start[i]) j = i;
+  const int tid = blockIdx.x - J.start[j];
+  const int R = J.R[j], Cc = J.Cc[j];
+  const int r0 = (tid / J.tiles_c[j]) * 64, c0 = (tid % J.tiles_c[j]) * 64;
   const int t = threadIdx.x;
+  // amax and scale of matrix j from its partials (same value in every block)
+  const float* pj = part + (long)j * AMAX_PARTS;
+  float m = fmaxf(fmaxf(pj[t], pj[t + 256]), fmaxf(pj[t + 512], pj[t + 768]));
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float mx = FMT == FP8_E5M2 ? 57344.0f : 448.0f;
+  const float s = amax > 0.0f ? mx / amax : 1.0f;
+  if (tid == 0 && t == 0) {
+    J.scal[j][0] = s;
+    J.scal[j][1] = amax;
+    J.scal[j][2] = 1.0f / s;
+  }
+  uint8_t* q = J.q[j];
+  uint8_t* qT = J.qT[j];
+  const bf16* x = J.x[j];
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const int rr = t / 8 + 32 * v, cc = 8 * (t % 8);
@@ -153,23 +218,23 @@ __global__ __launch_bounds__(256) void quant2d_k(int R, int Cc, const bf16* __re
   }
   if (!qT) return;
   __syncthreads();
-  // output row c0 + j of qT: bytes r0 + 16 g .. + 15 (source rows) of
-  // source column j; thread t: j = t / 4, g = t % 4
-  const int j = t / 4, g = t % 4;
-  if (c0 + j >= Cc) return;
+  // output row c0 + jj of qT: bytes r0 + 16 g .. + 15 (source rows) of
+  // source column jj; thread t: jj = t / 4, g = t % 4
+  const int jj = t / 4, g = t % 4;
+  const long ldT = J.ldT[j];
+  if (c0 + jj >= Cc || r0 + 16 * g >= ldT) return;
   uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t code = (tile[16 * g + 4 * k + e][j / 4] >> (8 * (j % 4))) & 0xffu;
+      const uint32_t code = (tile[16 * g + 4 * k + e][jj / 4] >> (8 * (jj % 4))) & 0xffu;
       word |= code << (8 * e);
     }
     w[k] = word;
   }
-  if (r0 + 16 * g < ldT)
-    *reinterpret_cast<uint4*>(qT + (long)(c0 + j) * ldT + r0 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(qT + (long)(c0 + jj) * ldT + r0 + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ------------------------------------------------------------ GEMM
@@ -326,21 +391,31 @@ hipError_t launch_fp8_gemm(int M, int N, int K, const void* A, long lda, int fa,
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_quantize_2d(int R, int Cc, const void* x, int fmt, void* q, void* qT, long ldT, float* scal,
-                                  float* part, hipStream_t s) {
-  if (R <= 0 || Cc <= 0 || Cc % 16 || (qT && (ldT < R || ldT % 64))) return hipErrorInvalidValue;
-  const long n = (long)R * Cc;
-  const long nb = fp8_amax_parts(n);
-  hipLaunchKernelGGL(amax_k, dim3((unsigned)nb), dim3(Q_THREADS), 0, s, n, (const bf16*)x, part);
-  hipLaunchKernelGGL(amax_finish_k, dim3(1), dim3(Q_THREADS), 0, s, (int)nb, (const float*)part, fmt, scal);
-  // with the transpose, the tiles cover the padded rows R .. ldT - 1 too (zeros)
-  const int rows = qT ? (int)ldT : R;
-  dim3 grid(cdiv(Cc, 64), cdiv(rows, 64));
+hipError_t launch_fp8_quantize_2d(const Fp8Q2d* d, int n, int fmt, float* part, hipStream_t s) {
+  if (n <= 0 || n > Q2D_MAX) return hipErrorInvalidValue;
+  Q2dJobs J{};
+  J.n = n;
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const Fp8Q2d& e = d[i];
+    if (e.R <= 0 || e.Cc <= 0 || e.Cc % 16 || (e.qT && (e.ldT < e.R || e.ldT % 64))) return hipErrorInvalidValue;
+    J.x[i] = static_cast<const bf16*>(e.x);
+    J.q[i] = static_cast<uint8_t*>(e.q);
+    J.qT[i] = static_cast<uint8_t*>(e.qT);
+    J.ldT[i] = e.ldT;
+    J.R[i] = e.R;
+    J.Cc[i] = e.Cc;
+    J.scal[i] = e.scal;
+    J.tiles_c[i] = cdiv(e.Cc, 64);
+    J.start[i] = tiles;
+    // with the transpose, the tiles cover the padded rows R .. ldT - 1 too (zeros)
+    tiles += J.tiles_c[i] * cdiv(e.qT ? e.ldT : (long)e.R, 64);
+  }
+  for (int i = n; i <= Q2D_MAX; ++i) J.start[i] = tiles;
+  hipLaunchKernelGGL(amax_parts_k, dim3(n * AMAX_PARTS), dim3(256), 0, s, J, part);
   if (fmt == FP8_E5M2)
-    hipLaunchKernelGGL(quant2d_k<FP8_E5M2>, grid, dim3(256), 0, s, R, Cc, (const bf16*)x, (const float*)scal,
-                       (uint8_t*)q, (uint8_t*)qT, ldT);
+    hipLaunchKernelGGL(quant2d_k<FP8_E5M2>, dim3(tiles), dim3(256), 0, s, J, (const float*)part);
   else
-    hipLaunchKernelGGL(quant2d_k<FP8_E4M3>, grid, dim3(256), 0, s, R, Cc, (const bf16*)x, (const float*)scal,
-                       (uint8_t*)q, (uint8_t*)qT, ldT);
+    hipLaunchKernelGGL(quant2d_k<FP8_E4M3>, dim3(tiles), dim3(256), 0, s, J, (const float*)part);
   return hipGetLastError();
 }

@@ -228,11 +228,21 @@ constexpr int FP8_E4M3 = 0, FP8_E5M2 = 1;
 long fp8_amax_parts(long n);
 // scal (device float[3]) <- scale, amax, 1 / scale; q <- codes; part: fp8_amax_parts(n) floats
 hipError_t launch_fp8_quantize(long n, const void* x, int fmt, void* q, float* scal, float* part, hipStream_t s);
-// A bf16 matrix x [R][Cc] (Cc a multiple of 16) quantized with one scale:
-// scal as above; q [R][Cc] codes (or NULL) and qT [Cc][ldT] transposed codes
-// (or NULL; ldT >= R a multiple of 64, columns R .. ldT - 1 zero).
-hipError_t launch_fp8_quantize_2d(int R, int Cc, const void* x, int fmt, void* q, void* qT, long ldT, float* scal,
-                                  float* part, hipStream_t s);
+// Up to Q2D_MAX bf16 matrices x [R][Cc] (Cc a multiple of 16) quantized to
+// one format, each with its own scale: scal as above; q [R][Cc] codes (or
+// NULL) and qT [Cc][ldT] transposed codes (or NULL; ldT >= R a multiple of
+// 64, columns R .. ldT - 1 zero).  part: fp8_q2d_parts(n) floats.
+constexpr int Q2D_MAX = 4;
+struct Fp8Q2d {
+  const void* x;
+  void* q;
+  void* qT;
+  long ldT;
+  int R, Cc;
+  float* scal;
+};
+constexpr long fp8_q2d_parts(int n) { return 1024L * n; }
+hipError_t launch_fp8_quantize_2d(const Fp8Q2d* d, int n, int fmt, float* part, hipStream_t s);
 // out (bf16, ldc) = A B^T * scal_a[2] * scal_b[2]; A [M][lda], B [N][ldb] codes, k contiguous
 hipError_t launch_fp8_gemm(int M, int N, int K, const void* A, long lda, int fa, const float* scal_a, const void* B,
                            long ldb, int fb, const float* scal_b, void* out, long ldc, hipStream_t s);
