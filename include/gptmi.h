@@ -128,7 +128,10 @@ size_t gpt_workspace_bytes(const gpt_config* cfg, int B, int T);
  *   y     [B*T, C] output (dtype).
  *   saved gpt_block_saved_bytes() bytes, filled for the backward (with the
  *         RoPE table it reads too); NULL runs inference only (intermediates
- *         then live in the workspace, which is otherwise not touched).
+ *         then live in the workspace).
+ *   ws    gpt_workspace_bytes() bytes of temporaries: the FP8 codes with
+ *         cfg->fp8, the intermediates when saved is NULL.  Where neither
+ *         applies the forward does not touch it and NULL is accepted.
  * Errors: INVALID (null pointer, B/T <= 0, T > block_size, n_embd % n_head,
  * odd head_dim with rope), UNSUPPORTED (head_dim not a multiple of 8 or
  * above 128, n_embd above 2048, or B*T*4*n_embd elements of 2 GiB or more:

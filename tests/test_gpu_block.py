@@ -98,6 +98,23 @@ def test_block_deterministic_and_causal(name):
     assert not torch.equal(ya[:, t + 1:], yb[:, t + 1:])
 
 
+@pytest.mark.parametrize("window", [0, 512])
+def test_block_deterministic_full(window):
+    """Bitwise run-to-run equality at the full d20 size (causal and
+    windowed), over four steps of one runner."""
+    w = synth.scaled(synth.D20_BLOCK, window=window)
+    print_case("block-deterministic-full", window)
+    x, dy, p, r = _run(w, False)
+    y1, dx1 = r.y.clone(), r.dx.clone()
+    g1 = {k: v.clone() for k, v in r.g.items() if v is not None}
+    for _ in range(3):
+        r.step()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, r.y) and torch.equal(dx1, r.dx)
+        for k, v in g1.items():
+            assert torch.equal(v, r.g[k]), k
+
+
 @pytest.mark.parametrize("name,window", [("d20_block", 70), ("gpt2_block", 130)])
 def test_block_window_locality(name, window):
     """Bitwise: with a window of W keys, changing the inputs at positions
