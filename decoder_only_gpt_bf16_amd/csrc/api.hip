@@ -530,8 +530,17 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
     return GPT_OK;
   };
 
-  if (cfg->rope) RUN("rope_table", launch_rope_table(T, d.D, cfg->rope_base, cs, s));
-  RUN("norm1_fwd", launch_norm_fwd(ty, kind, d.N, C, x, w->ln1_w, opt(cfg, w->ln1_b), cfg->norm_eps, sv.a1, sv.stats1, s));
+  // norm1's launch also writes the RoPE table (positions 0..T-1) for the
+  // QKV epilogue and the backward; theta_i = base^(-2i/D) in double
+  RopeJob rope{};
+  if (cfg->rope) {
+    rope.cs = cs;
+    rope.T = T;
+    rope.half = d.D / 2;
+    for (int i = 0; i < rope.half; ++i) rope.theta[i] = std::pow((double)cfg->rope_base, -2.0 * i / d.D);
+  }
+  RUN("norm1_fwd", launch_norm_fwd(ty, kind, d.N, C, x, w->ln1_w, opt(cfg, w->ln1_b), cfg->norm_eps, sv.a1, sv.stats1, s,
+                                   &rope));
   // RoPE / QK-norm ride in the QKV GEMM's epilogue when a wave's 128 output
   // columns are exactly one head (bf16, head_dim 128); else a separate pass
   const bool qk = cfg->rope || cfg->qk_norm;

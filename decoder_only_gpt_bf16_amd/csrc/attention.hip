@@ -963,26 +963,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_simt(int TT, int H, const T*
 }
 
 // ----------------------------------------------------- RoPE / QK-norm, delta
-// cs[t][i] = (cos, sin)(t theta_i), theta_i = base^(-2 i / D).  The block's
-// frequencies are computed once in double; each angle t theta_i is formed
-// and reduced to [-pi, pi] in double, so the float sincos that follows is
-// accurate to a few ulp for any position.
-__global__ __launch_bounds__(256) void rope_table_k(int T, int D, double base, float2* cs) {
-  __shared__ double th[256];
-  const int half = D / 2;
-  if ((int)threadIdx.x < half) th[threadIdx.x] = pow(base, -2.0 * threadIdx.x / D);
-  __syncthreads();
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * half) return;
-  const int t = idx / half, i = idx % half;
-  constexpr double TWO_PI = 6.283185307179586476925286766559;
-  const double a = (double)t * th[i];
-  const float r = (float)(a - TWO_PI * rint(a * (1.0 / TWO_PI)));
-  float sn, c;
-  sincosf(r, &sn, &c);
-  cs[idx] = make_float2(c, sn);
-}
-
+// (the RoPE table itself is written by the norm1 launch: rope_entry)
 // One wavefront per (row, head, q|k); lane i < D/2 handles pair (i, i + D/2).
 template <typename T>
 __global__ __launch_bounds__(256) void qk_fwd_k(int N, int TT, int H, int D, int rope, int qk_norm, float eps,
@@ -1108,12 +1089,6 @@ hipError_t simt_dispatch(int which, int B, int TT, int H, int D, const void* qkv
 }  // namespace
 
 bool attn_mfma_supported(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
-
-hipError_t launch_rope_table(int T, int D, float base, float2* cs, hipStream_t s) {
-  const int n = T * (D / 2);
-  hipLaunchKernelGGL(rope_table_k, dim3(cdiv(n, 256)), dim3(256), 0, s, T, D, (double)base, cs);
-  return hipGetLastError();
-}
 
 hipError_t launch_qk_fwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm, float eps,
                          const float2* cs, void* qkv, float* rstd, hipStream_t s) {

@@ -34,6 +34,27 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// The RoPE (cos, sin) table [T][D / 2], written by a kernel that runs anyway
+// before its readers (cs == nullptr: none).  Entry (t, i) is the angle
+// t * theta_i, theta_i = base^(-2i/D) (given in double), formed and reduced
+// to [-pi, pi] in double, then the float sincos of the residue: a few ulp
+// at any position.
+constexpr int ROPE_MAX_HALF = 64;
+struct RopeJob {
+  float2* cs;
+  int T, half;
+  double theta[ROPE_MAX_HALF];
+};
+__device__ __forceinline__ float2 rope_entry(const RopeJob& rj, int e) {
+  constexpr double TWO_PI = 6.283185307179586476925286766559;
+  const int t = e / rj.half, i = e - t * rj.half;
+  const double a = (double)t * rj.theta[i];
+  const float r = (float)(a - TWO_PI * rint(a * (1.0 / TWO_PI)));
+  float sn, c;
+  sincosf(r, &sn, &c);
+  return make_float2(c, sn);
+}
+
 // Vector of 8 storage elements converted to/from fp32.
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {

@@ -112,8 +112,10 @@ hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size
 // ---------------------------------------------------------------------------
 // Norms, embeddings, attention, cross-entropy, reductions.
 // ---------------------------------------------------------------------------
+// rope (optional): the same launch also writes that RoPE table.
 hipError_t launch_norm_fwd(int dtype, int kind, int N, int C, const void* x, const void* w,
-                           const void* b, float eps, void* y, float* stats, hipStream_t s);
+                           const void* b, float eps, void* y, float* stats, hipStream_t s,
+                           const RopeJob* rope = nullptr);
 // dx = norm_bwd(dy) (+ resid); column partial sums of dy*xhat and dy into
 // colpart [2][nblk][C] (when want_cols), reduced by launch_colsum_finish.
 hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, const void* w,
@@ -138,7 +140,6 @@ hipError_t launch_embed_bwd(int dtype, int B, int T, int C, int V, int wpe_rows,
                             size_t scratch_bytes, hipStream_t s);
 
 // RoPE angle table: cs[t * (D/2) + i] = (cos, sin)(t * base^(-2i/D)).
-hipError_t launch_rope_table(int T, int D, float base, float2* cs, hipStream_t s);
 // In place on the q and k thirds of qkv [N, 3C]: RoPE then QK-norm; saves
 // 1/rms of q and k per (row, head) into rstd [2][N][H] when qk_norm.
 hipError_t launch_qk_fwd(int dtype, int B, int T, int H, int D, int rope, int qk_norm, float eps,

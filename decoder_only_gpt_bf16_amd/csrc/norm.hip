@@ -9,23 +9,44 @@ namespace {
 constexpr int ROWS_PER_BLOCK = 4;  // one row per wave, 4 waves per block
 constexpr int MAX_VPL = 4;         // up to 64 * 8 * 4 = 2048 columns
 
-template <typename T, int KIND>
+template <typename T, int KIND, bool ROPE>
 __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restrict__ x,
                                                   const T* __restrict__ w, const T* __restrict__ b,
-                                                  float eps, T* __restrict__ y, float* __restrict__ stats) {
+                                                  float eps, T* __restrict__ y, float* __restrict__ stats,
+                                                  RopeJob rj) {
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= N) return;
   const T* xr = x + (long)row * C;
   float v[MAX_VPL][8];
   float s = 0.0f;
+  if constexpr (ROPE) {
 #pragma unroll
-  for (int i = 0; i < MAX_VPL; ++i) {
-    const int c = (lane + 64 * i) * 8;
-    if (c < C) {
-      Vec8<T>::load(xr + c, v[i]);
+    for (int i = 0; i < MAX_VPL; ++i) {
+      const int c = (lane + 64 * i) * 8;
+      if (row < N && c < C) Vec8<T>::load(xr + c, v[i]);
+    }
+    // the RoPE table while the row's loads are in flight
+    const int n = rj.T * rj.half, nthr = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += nthr) rj.cs[e] = rope_entry(rj, e);
+    if (row >= N) return;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[i][e];
+    for (int i = 0; i < MAX_VPL; ++i) {
+      const int c = (lane + 64 * i) * 8;
+      if (c < C) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[i][e];
+      }
+    }
+  } else {
+    if (row >= N) return;
+#pragma unroll
+    for (int i = 0; i < MAX_VPL; ++i) {
+      const int c = (lane + 64 * i) * 8;
+      if (c < C) {
+        Vec8<T>::load(xr + c, v[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[i][e];
+      }
     }
   }
   const float mean = KIND == 0 ? wave_sum(s) / C : 0.0f;
@@ -227,13 +248,18 @@ constexpr int COLSUM_ROWS = 64;
 int norm_bwd_blocks(int N) { return std::max(1, std::min(cdiv(N, ROWS_PER_BLOCK), 1024)); }
 
 hipError_t launch_norm_fwd(int dtype, int kind, int N, int C, const void* x, const void* w,
-                           const void* b, float eps, void* y, float* stats, hipStream_t s) {
+                           const void* b, float eps, void* y, float* stats, hipStream_t s, const RopeJob* rope) {
   if (N <= 0) return hipSuccess;
   dim3 grid(cdiv(N, ROWS_PER_BLOCK)), block(256);
-#define NF(T, K) hipLaunchKernelGGL((norm_fwd_k<T, K>), grid, block, 0, s, N, C, (const T*)x, \
-                                    (const T*)w, (const T*)b, eps, (T*)y, stats)
-  if (dtype == 1) { if (kind == 0) NF(bf16, 0); else NF(bf16, 1); }
-  else { if (kind == 0) NF(float, 0); else NF(float, 1); }
+  RopeJob rj{};
+  const bool r = rope && rope->cs;
+  if (r) rj = *rope;
+#define NF(T, K, R) hipLaunchKernelGGL((norm_fwd_k<T, K, R>), grid, block, 0, s, N, C, (const T*)x, \
+                                       (const T*)w, (const T*)b, eps, (T*)y, stats, rj)
+#define NFR(T, K) do { if (r) NF(T, K, true); else NF(T, K, false); } while (0)
+  if (dtype == 1) { if (kind == 0) NFR(bf16, 0); else NFR(bf16, 1); }
+  else { if (kind == 0) NFR(float, 0); else NFR(float, 1); }
+#undef NFR
 #undef NF
   return hipGetLastError();
 }
