@@ -33,12 +33,31 @@ SITE_KERNEL = {
     "attn_fwd": (["attn_fwd_mfma<128, true>"], "attention"),
     "attn_bwd_dkdv": (["attn_bwd_dkdv_mfma<128>"], "attention"),
     "attn_bwd_dq": (["attn_bwd_dq_mfma<128>"], "attention"),
-    "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 2>"], "gemm"),
-    "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4>"], "gemm"),
-    "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4>"], "gemm"),
+    "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 2, 0>"], "gemm"),
+    "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4, 0>"], "gemm"),
+    "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4, 0>"], "gemm"),
     "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2>", "streamk_fixup<256, 256>"], "gemm"),
+    "weight_transpose": (["transpose_bf16_k"], "gemm"),
+    # rocprofv3 prints the bf16 instances of the norm kernels this way
+    "norm1_fwd": (["norm_fwd_k<bool _Accum, int, E, true>"], "norm"),
+    "norm2_fwd": (["norm_fwd_k<bool _Accum, int, E, false>"], "norm"),
+    # the two backward norms are one instance at one shape
+    "norm1_bwd": (["norm_bwd_k<bool _Accum, int, E, false>"], "norm"),
+    "norm2_bwd": (["norm_bwd_k<bool _Accum, int, E, false>"], "norm"),
 }
-SOURCES = {"attention": ["attention.hip", "common.h", "kernels.h"], "gemm": ["gemm.hip", "common.h", "kernels.h"]}
+SOURCES = {"attention": ["attention.hip", "common.h", "kernels.h"], "gemm": ["gemm.hip", "common.h", "kernels.h"],
+           "xent": ["xent.hip", "common.h", "kernels.h"], "norm": ["norm.hip", "common.h", "kernels.h"]}
+# the LM heads: one counter summary per head (their kernels are shared, with
+# other shapes), call site -> kernels as for the block
+HEAD_PROFILES = {name: os.path.join(HERE, "profiles", f"hbm_traffic_{name}.md")
+                 for name in ("gpt2_124m_step_head", "d20_val_bpb_head")}
+HEAD_SITE_KERNEL = {
+    "xent_stats_gemm": (["gemm_mfma<false, false, 4, 256, 256, 8, 2, 0>"], "gemm"),
+    "xent_grad_gemm": (["gemm_mfma<false, false, 5, 256, 256, 8, 2, 0>"], "gemm"),
+    "xent_dh_gemm": (["gemm_mfma<false, true, 3, 128, 128, 4, 2, 0>"], "gemm"),
+    "xent_finish": (["xent_finish_k"], "xent"),
+    "xent_dh_convert": (["_ZN12_GLOBAL__N_18f32_to_kIDF16bEEvlPKfPT_"], "xent"),
+}
 
 
 def block_flops(B, T, C, H):
@@ -88,17 +107,18 @@ def source_hash(family):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(site):
+def measured_traffic(site, profile=TRAFFIC_PROFILE, table=None):
     """HBM bytes per launch of a call site's kernel (FETCH_SIZE + WRITE_SIZE,
-    copy-calibrated) from the committed counter summary, or None when the
+    copy-calibrated) from a committed counter summary, or None when the
     site's kernel is not uniquely named there or its sources changed since
     the counters were taken."""
-    if site not in SITE_KERNEL or not os.path.exists(TRAFFIC_PROFILE):
+    table = SITE_KERNEL if table is None else table
+    if site not in table or not os.path.exists(profile):
         return None
-    kernels, fam = SITE_KERNEL[site]
+    kernels, fam = table[site]
     want = source_hash(fam)
     found = {}
-    with open(TRAFFIC_PROFILE) as fh:
+    with open(profile) as fh:
         for line in fh:
             cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
             if len(cells) == 6 and cells[0] in kernels:
@@ -108,30 +128,63 @@ def measured_traffic(site):
     return sum(found.values()) if len(found) == len(kernels) else None
 
 
-def cpu_baseline(w, min_s=12.0):
+def cpu_baseline(w, run_s=4.0, runs=3):
     """The float64 oracle on whole sequences of the workload, one at a time
-    (sequence b of the same seeded batch), until at least min_s seconds of CPU
-    work have run."""
-    import numpy as np
+    (sequence b of the same seeded batch): `runs` runs of at least run_s
+    seconds each on the BLAS thread pool as configured, whose median is the
+    value; then, with one BLAS thread, one sequence of the GPT-2 and d20
+    blocks and one whole tiny-model step (loss and every gradient)."""
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         cores = len(os.sched_getaffinity(0))
     import oracle as O
     from decoder_only_gpt_bf16_amd import synth
-    x, dy, p = synth.make_block_inputs(w)
-    cfg = synth.oracle_cfg(w.cfg)
-    n, dt = 0, 0.0
-    t0 = time.perf_counter()
-    while dt < min_s:
-        b = n % w.B
-        y, cache = O.block_fwd(cfg, x[b:b + 1], p)
-        O.block_bwd(cfg, dy[b:b + 1], cache, p)
-        n += 1
-        dt = time.perf_counter() - t0
-    return {"value": n * w.T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} sequences (B=1, T={w.T} each) of the d20 block fwd+bwd in float64 NumPy, {dt:.1f} s"}
+
+    def block_seqs(wl, min_s):
+        x, dy, p = synth.make_block_inputs(wl)
+        cfg = synth.oracle_cfg(wl.cfg)
+        n, dt = 0, 0.0
+        t0 = time.perf_counter()
+        while n == 0 or dt < min_s:
+            b = n % wl.B
+            y, cache = O.block_fwd(cfg, x[b:b + 1], p)
+            O.block_bwd(cfg, dy[b:b + 1], cache, p)
+            n += 1
+            dt = time.perf_counter() - t0
+        return n, dt
+
+    rates, total_n, total_s = [], 0, 0.0
+    for _ in range(runs):
+        n, dt = block_seqs(w, run_s)
+        rates.append(n * w.T / dt)
+        total_n += n
+        total_s += dt
+    rates.sort()
+    out = {"value": rates[len(rates) // 2], "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "runs": [round(r, 1) for r in rates],
+           "sample": f"median of {runs} runs of >= {run_s:.0f} s, {total_n} sequences (B=1, T={w.T} each) of the "
+                     f"d20 block fwd+bwd in float64 NumPy, {total_s:.1f} s in all"}
+    if threadpool_limits is not None:
+        single = {}
+        with threadpool_limits(1):
+            for name in ("gpt2_block", "d20_block"):
+                wl = synth.BY_NAME[name]
+                n, dt = block_seqs(wl, 0.0)
+                single[name] = {"tokens_per_s": round(n * wl.T / dt, 1), "seconds": round(dt, 2),
+                                "sample": f"one sequence (T={wl.T}) fwd+bwd"}
+            wl = synth.TINY
+            ids, y, P, _ = synth.make_model_inputs(wl)
+            cfg = synth.oracle_cfg(wl.cfg)
+            t0 = time.perf_counter()
+            O.model_fwd_bwd(cfg, ids, y, P)
+            dt = time.perf_counter() - t0
+            single[wl.name] = {"tokens_per_s": round(wl.B * wl.T / dt, 1), "seconds": round(dt, 4),
+                               "sample": f"one whole step (B={wl.B}, T={wl.T})"}
+        out["single_thread"] = single
+    return out
 
 
 def time_steps(fn, steps, warmup, per_step=None):
@@ -175,6 +228,8 @@ def main():
                     help="also time FP8 quantization, FP8 GEMMs at the d20 Linear shapes and the FP8 d20 block step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
+    ap.add_argument("--head-only", choices=sorted(HEAD_PROFILES),
+                    help="time only this LM head (for profiling it alone) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (data-parallel sharding "
@@ -194,6 +249,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.head_only:
+        print(json.dumps({"lm_head": lm_head_workloads(args, only=args.head_only)}), flush=True)
+        return
 
     w = synth.D20_BLOCK
     cfg = w.cfg
@@ -220,6 +279,10 @@ def main():
         if bound:
             e["bound"] = bound
             e["frac"] = (work / (avg * 1e-6)) / (PEAK_BF16 if bound == "mfma" else PEAK_HBM)
+            e["algorithmic"] = work
+        tr = measured_traffic(name)
+        if tr is not None:
+            e["traffic"] = tr
         sites[name] = e
     total_us = sum(us for _, us in trace.values())
     for name, (n, us) in trace.items():
@@ -468,7 +531,7 @@ def head_site_work(name, N, C, Vc, P):
     return None, None
 
 
-def lm_head_workloads(args):
+def lm_head_workloads(args, only=None):
     """The vocabulary-chunked LM head with softmax cross-entropy at the two
     full-size heads: the GPT-2 124M step (N 16384, C 768, tied V 50304:
     forward + backward: statistics, logit gradient, dh and dW per chunk of
@@ -485,6 +548,8 @@ def lm_head_workloads(args):
     res = {}
     gen = torch.Generator(device="cuda").manual_seed(7)
     for name, w, grad in (("gpt2_124m_step_head", synth.GPT2_STEP, True), ("d20_val_bpb_head", synth.D20_EVAL, False)):
+        if only is not None and name != only:
+            continue
         cfg, N = w.cfg, w.B * w.T
         C, V = cfg.n_embd, cfg.vocab_size
         c = B.make_config(cfg)
@@ -515,7 +580,7 @@ def lm_head_workloads(args):
             if bound:
                 e["bound"] = bound
                 e["frac"] = round(work / (avg * 1e-6) / (PEAK_BF16 if bound == "mfma" else PEAK_HBM), 4)
-                tr = measured_traffic(site)
+                tr = measured_traffic(site, HEAD_PROFILES[name], HEAD_SITE_KERNEL)
                 if tr is not None:
                     e["traffic"] = tr
             sites[site] = e
