@@ -230,6 +230,8 @@ def main():
                     help="first run 4 device copies of 256 MiB (known HBM bytes) to scale the HBM counters")
     ap.add_argument("--head-only", choices=sorted(HEAD_PROFILES),
                     help="time only this LM head (for profiling it alone) and print its figures")
+    ap.add_argument("--config-only", choices=["gpt2_block", "gpt2_124m_step", "d20_val_bpb"],
+                    help="time only this other configuration (for profiling it alone) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (data-parallel sharding "
@@ -252,6 +254,9 @@ def main():
 
     if args.head_only:
         print(json.dumps({"lm_head": lm_head_workloads(args, only=args.head_only)}), flush=True)
+        return
+    if args.config_only:
+        print(json.dumps({"configs": config_workloads(args, only=args.config_only)}), flush=True)
         return
 
     w = synth.D20_BLOCK
@@ -465,28 +470,42 @@ def adamw_workload(args):
     return res
 
 
-def config_workloads(args):
+def config_workloads(args, only=None):
     """The other configurations at their full sizes: the GPT-2 124M block
     fwd+bwd (B 8, T 1024), the 12-layer GPT-2 124M training step (B 16,
     T 1024, tied head V 50304) and the 20-layer d20 val-bpb evaluation (B 8,
     T 2048, untied head V 32768, forward only).  Useful FLOPs: 6 per
     parameter-FLOP of the Linear layers and the head, causal attention on the
     lower triangle."""
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import BlockRunner
+    res = {}
+    want = lambda w: only is None or w.name == only  # noqa: E731
+    w = synth.GPT2_BLOCK
+    if want(w):
+        x, dy, p = synth.make_block_inputs(w)
+        r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
+        per = []
+        ms = time_steps(r.step, args.steps, args.warmup, per)
+        f = block_flops(w.B, w.T, w.cfg.n_embd, w.cfg.n_head)
+        res[w.name] = {"tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1), "ms": round(ms, 4),
+                       "ms_median": round(sorted(per)[len(per) // 2], 4),
+                       "mfma_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4), "flop_per_step": f}
+        del r
+    w = synth.GPT2_STEP
+    if want(w):
+        res.update(_gpt2_step(args, w))
+    w = synth.D20_EVAL
+    if want(w):
+        res.update(_d20_eval(args, w))
+    return res
+
+
+def _gpt2_step(args, w):
     import torch
     from decoder_only_gpt_bf16_amd import synth
-    from decoder_only_gpt_bf16_amd.model import BlockRunner, ModelRunner
+    from decoder_only_gpt_bf16_amd.model import ModelRunner
     res = {}
-    w = synth.GPT2_BLOCK
-    x, dy, p = synth.make_block_inputs(w)
-    r = BlockRunner(w.cfg, w.B, w.T, x, dy, p)
-    per = []
-    ms = time_steps(r.step, args.steps, args.warmup, per)
-    f = block_flops(w.B, w.T, w.cfg.n_embd, w.cfg.n_head)
-    res[w.name] = {"tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1), "ms": round(ms, 4),
-                   "ms_median": round(sorted(per)[len(per) // 2], 4), "mfma_frac": round(f / (ms * 1e-3) / PEAK_BF16, 4),
-                   "flop_per_step": f}
-    del r
-    w = synth.GPT2_STEP
     ids, y, P, tb = synth.make_model_inputs(w)
     m = ModelRunner(w.cfg, w.B, w.T, P, tb)
     m.set_batch(ids, y)
@@ -499,7 +518,14 @@ def config_workloads(args):
                    "flop_per_step": f, "loss": m.loss.item()}
     del m, P
     torch.cuda.empty_cache()
-    w = synth.D20_EVAL
+    return res
+
+
+def _d20_eval(args, w):
+    import torch
+    from decoder_only_gpt_bf16_amd import synth
+    from decoder_only_gpt_bf16_amd.model import ModelRunner
+    res = {}
     ids, y, P, tb = synth.make_model_inputs(w)
     m = ModelRunner(w.cfg, w.B, w.T, P, tb, train=False)
     m.set_batch(ids, y)
