@@ -37,7 +37,6 @@ SITE_KERNEL = {
     "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4, 0>"], "gemm"),
     "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4, 0>"], "gemm"),
     "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2>", "streamk_fixup<256, 256>"], "gemm"),
-    "weight_transpose": (["transpose_bf16_k"], "gemm"),
     # rocprofv3 prints the bf16 instances of the norm kernels this way
     "norm1_fwd": (["norm_fwd_k<bool _Accum, int, E, true>"], "norm"),
     "norm2_fwd": (["norm_fwd_k<bool _Accum, int, E, false>"], "norm"),

@@ -149,7 +149,12 @@ struct Saved {
   // weights [In][Out] for the backward's GEMMs
   float* f8sc;
   uint8_t *qa1T, *qoT, *qa2T, *qgT, *qWqkvT, *qWoT, *qWfcT, *qWprojT;
+  // bf16 GEMMs: transposed copies of W_fc [C][4C], W_o [C][C] and W_qkv
+  // [C][3C], written by the forward, read by the backward's input gradients
+  void *wt_fc, *wt_o, *wt_qkv;
 };
+// the bf16 (non-FP8) block keeps transposed weights in `saved`
+bool keeps_wt(const Dims& d, const gpt_config* cfg) { return d.dtype == GPT_DTYPE_BF16 && !cfg->fp8; }
 
 // tokens padded to whole 64-row tiles of the transposed codes
 long fp8_np(long N) { return (N + 63) / 64 * 64; }
@@ -182,6 +187,11 @@ Saved saved_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
     s.qWfcT = a.take_n<uint8_t>(C * fp8_ld64(4 * C));
     s.qWprojT = a.take_n<uint8_t>(4 * C * fp8_ld64(C));
   }
+  if (keeps_wt(d, cfg)) {
+    s.wt_fc = a.take(4 * C * C * es);
+    s.wt_o = a.take(C * C * es);
+    s.wt_qkv = a.take(3 * C * C * es);
+  }
   return s;
 }
 
@@ -207,7 +217,6 @@ Fp8FwdWs fp8_fwd_layout(const Dims& d, Arena& a) {
 struct BwdWs {
   void *du, *da, *dx1, *dO, *dqkv;
   float *delta, *colpart, *colsum, *split;
-  void *wt_fc, *wt_o, *wt_qkv;  // bf16: transposed weights for the input gradients
   // FP8: codes of the current gradient [N][Out] and their transpose
   // [Out][Np], amax partials, the gradients' scales [4][4]
   uint8_t *qg, *qgT;
@@ -302,11 +311,6 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   w.colpart = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
   w.colsum = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, 4 * C)));
   w.split = static_cast<float*>(a.take(split_need(d, cfg)));
-  if (d.dtype == GPT_DTYPE_BF16 && !cfg->fp8) {
-    w.wt_fc = a.take(4 * C * C * es);
-    w.wt_o = a.take(C * C * es);
-    w.wt_qkv = a.take(3 * C * C * es);
-  }
   if (cfg->fp8) {
     w.qg = a.take_n<uint8_t>(N * 4 * C);
     w.qgT = a.take_n<uint8_t>(4 * C * fp8_np(N));
@@ -554,7 +558,12 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x, const gpt_
   if ((st = linear("qkv_gemm", g, 0, sv.qa1T, 0))) return st;
   if (qk && !qk_fused)
     RUN("qk_rope_norm", launch_qk_fwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, cfg->norm_eps, cs, sv.qkv, sv.qkr, s));
-  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, cfg->attn_window, sv.qkv, sv.o, sv.lse, s));
+  // the backward's transposed weights ride in the attention launch, whose
+  // tail has CUs to spare (training only: inference needs none)
+  const bool wt = saved && keeps_wt(d, cfg);
+  const TransposeDesc td[3] = {{w->w_fc, sv.wt_fc, 4 * C, C}, {w->w_o, sv.wt_o, C, C}, {w->w_qkv, sv.wt_qkv, 3 * C, C}};
+  RUN("attn_fwd", launch_attn_fwd(ty, B, T, d.H, d.D, cfg->qk_norm, cfg->attn_window, sv.qkv, sv.o, sv.lse, td,
+                                  wt ? 3 : 0, s));
   g = lin_fwd(d, sv.o, C, w->w_o, C, EPI_STORE);
   g.out = sv.x1; g.ldc = C; g.bias = opt(cfg, w->b_o); g.resid = x; g.ldr = C;
   if ((st = linear("out_gemm", g, 2, sv.qoT, 1))) return st;
@@ -627,14 +636,11 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     return GPT_OK;
   };
 
-  // bf16: the input gradients through W_fc, W_o and W_qkv read transposed
-  // copies (k contiguous on both sides of those GEMMs); W_proj's is read as
-  // it lies (its wide tiles run as fast either way)
-  const bool wt = ty == GPT_DTYPE_BF16 && !f8;
-  if (wt) {
-    const TransposeDesc td[3] = {{w->w_fc, b.wt_fc, 4 * C, C}, {w->w_o, b.wt_o, C, C}, {w->w_qkv, b.wt_qkv, 3 * C, C}};
-    RUN("weight_transpose", launch_transpose(td, 3, s));
-  }
+  // bf16: the input gradients through W_fc, W_o and W_qkv read the
+  // transposed copies the forward left in `saved` (k contiguous on both
+  // sides of those GEMMs); W_proj's is read as it lies (its wide tiles run
+  // as fast either way)
+  const bool wt = keeps_wt(d, cfg);
   // weight gradients depend on nothing computed later: in bf16 they are
   // gathered and run as one grouped launch at the end of the backward (one
   // launch fills the machine where each alone would leave CUs idle)
@@ -652,7 +658,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
   }
   if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
-  g = wt ? lin_dgrad_t(d, b.du, 4 * C, b.wt_fc, C, EPI_STORE) : lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
+  g = wt ? lin_dgrad_t(d, b.du, 4 * C, sv.wt_fc, C, EPI_STORE) : lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   if (f8) {
     if ((st = fp8_grad(b.du, 4 * C, 1))) return st;
@@ -670,7 +676,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     if (cfg->bias) RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln2_b, accumulate, s));
   }
   // attention output projection
-  g = wt ? lin_dgrad_t(d, b.dx1, C, b.wt_o, C, EPI_STORE) : lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
+  g = wt ? lin_dgrad_t(d, b.dx1, C, sv.wt_o, C, EPI_STORE) : lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
   g.out = b.dO; g.ldc = C;
   if (f8) {
     if ((st = fp8_grad(b.dx1, C, 2))) return st;
@@ -699,7 +705,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
       RUN("qk_bwd", launch_qk_bwd(ty, B, T, d.H, d.D, cfg->rope, cfg->qk_norm, sv.cs, sv.qkv, sv.qkr, b.dqkv, s));
   }
   // fused QKV projection
-  g = wt ? lin_dgrad_t(d, b.dqkv, 3 * C, b.wt_qkv, C, EPI_STORE)
+  g = wt ? lin_dgrad_t(d, b.dqkv, 3 * C, sv.wt_qkv, C, EPI_STORE)
          : lin_dgrad(d, b.dqkv, 3 * C, w->w_qkv, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   if (f8) {

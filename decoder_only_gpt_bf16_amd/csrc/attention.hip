@@ -225,16 +225,26 @@ __device__ __forceinline__ void attn_block(int T, int H, int& rank, int& h, int&
 // every exponent uses that constant shift instead of a running maximum:
 // softmax is shift-invariant, and with QK-norm |q . k| <= |q| |k| <= D bounds
 // the scaled score by sqrt(D), so exp2 neither overflows nor underflows.
+// side / nattn: blocks nattn.. of the grid run the transpose jobs `side`
+// instead (work that does not depend on the attention): dispatched after
+// every attention block, they fill the CUs that the short query blocks free
+// while the long ones finish.
 template <int D, bool FIXED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(int T, int H, const bf16* __restrict__ qkv,
                                                         bf16* __restrict__ o, float* __restrict__ lse,
-                                                        float scale_log2, float shift_log2, int W) {
+                                                        float scale_log2, float shift_log2, int W,
+                                                        const TransposeJobs side, int nattn) {
   constexpr int KS = D / 16, DT = D / 32, KU = D / 8;
   __shared__ uint4 sK[2][64 * KU];
   __shared__ uint4 sV[2][64 * KU];
+  if ((int)blockIdx.x >= nattn) {
+    transpose_block(side, blockIdx.x - nattn);
+    return;
+  }
   const int nqb = (T + 127) / 128;
-  int rank, h, b;
-  attn_block(T, H, rank, h, b);
+  const int HB = nattn / nqb;
+  const int rank = blockIdx.x / HB, bh = blockIdx.x - rank * HB;
+  const int h = bh % H, b = bh / H;
   const int qb = nqb - 1 - rank;
   const int C = H * D;
   const long ld = 3L * C;
@@ -1117,16 +1127,20 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
 }
 
 hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, int window, const void* qkv,
-                           void* o, float* lse, hipStream_t s) {
+                           void* o, float* lse, const TransposeDesc* side, int nside, hipStream_t s) {
   const int W = window >= T ? 0 : window;  // a window of T or more keys is the full causal mask
   if (attn_mfma_supported(dtype, D)) {
     const float scale_log2 = LOG2E / sqrtf((float)D);
     // with QK-norm |q|, |k| <= sqrt(D) (up to bf16 rounding), so a scaled
     // score is at most sqrt(D); the shift adds 3% for the rounding
     const float shift_log2 = 1.03f * sqrtf((float)D) * LOG2E;
-    dim3 grid(cdiv(T, 128) * H * B);
+    if (nside < 0 || nside > TRANSPOSE_MAX) return hipErrorInvalidValue;
+    TransposeJobs J{};
+    const int nj = nside ? make_transpose_jobs(side, nside, J) : 0;
+    const int nattn = cdiv(T, 128) * H * B;
+    dim3 grid(nattn + nj);
 #define AF(DD, FX) hipLaunchKernelGGL((attn_fwd_mfma<DD, FX>), grid, dim3(256), 0, s, T, H, (const bf16*)qkv, \
-                                      (bf16*)o, lse, scale_log2, shift_log2, W)
+                                      (bf16*)o, lse, scale_log2, shift_log2, W, J, nattn)
     if (D == 128) {
       if (qk_norm) AF(128, true); else AF(128, false);
     } else {
@@ -1135,8 +1149,10 @@ hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, i
 #undef AF
     return hipGetLastError();
   }
-  if (dtype == 1) return simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s);
-  return simt_dispatch<float>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s);
+  hipError_t e = dtype == 1 ? simt_dispatch<bf16>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s)
+                            : simt_dispatch<float>(0, B, T, H, D, qkv, nullptr, o, lse, nullptr, W, s);
+  if (e == hipSuccess && nside) e = launch_transpose(side, nside, s);
+  return e;
 }
 
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO, float* delta,

@@ -1023,48 +1023,7 @@ GemmParams make_params(const GemmDesc& d) {
 }
 
 // ---------------------------------------------------------------- transpose
-// dst[c][r] = src[r][c] for up to TRANSPOSE_MAX bf16 matrices in one launch
-// (blocks [start[j], start[j + 1]) cover matrix j in 64-row x 256-column
-// tiles).  A thread moves one 8 x 8 block: 8 row vectors of 16 bytes in,
-// transposed in registers (halves of 32-bit words regrouped), 8 row vectors
-// of the transpose out.  A wave covers 64 x 64 elements as 8 x 8 such
-// blocks, so that both its loads and its stores are whole 128-byte rows of
-// 8 lanes.  Row and column counts are multiples of 8.
-struct TransposeJobs {
-  const bf16* src[TRANSPOSE_MAX];
-  bf16* dst[TRANSPOSE_MAX];
-  int rows[TRANSPOSE_MAX], cols[TRANSPOSE_MAX], tiles_c[TRANSPOSE_MAX];
-  int start[TRANSPOSE_MAX + 1];
-  int n;
-};
-
-__global__ __launch_bounds__(256) void transpose_bf16_k(TransposeJobs J) {
-  int j = 0;
-  while (j + 1 < J.n && (int)blockIdx.x >= J.start[j + 1]) ++j;
-  const int tid = blockIdx.x - J.start[j];
-  const int R = J.rows[j], Cc = J.cols[j];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = (tid / J.tiles_c[j]) * 64 + 8 * (lane >> 3);
-  const int c = (tid % J.tiles_c[j]) * 256 + 64 * wave + 8 * (lane & 7);
-  if (r >= R || c >= Cc) return;
-  const bf16* src = J.src[j] + (long)r * Cc + c;
-  uint4 in[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const uint4*>(src + (long)i * Cc);
-  bf16* dst = J.dst[j] + (long)c * R + r;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    // output row q (source column q): word k pairs source rows 2k and 2k + 1
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * k])[q >> 1];
-      const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * k + 1])[q >> 1];
-      w[k] = (q & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    *reinterpret_cast<uint4*>(dst + (long)q * R) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
+__global__ __launch_bounds__(256) void transpose_bf16_k(TransposeJobs J) { transpose_block(J, blockIdx.x); }
 
 }  // namespace
 
@@ -1314,17 +1273,7 @@ hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size
 hipError_t launch_transpose(const TransposeDesc* d, int n, hipStream_t s) {
   if (n <= 0 || n > TRANSPOSE_MAX) return hipErrorInvalidValue;
   TransposeJobs J{};
-  J.n = n;
-  J.start[0] = 0;
-  for (int i = 0; i < n; ++i) {
-    J.src[i] = static_cast<const bf16*>(d[i].src);
-    J.dst[i] = static_cast<bf16*>(d[i].dst);
-    J.rows[i] = d[i].rows;
-    J.cols[i] = d[i].cols;
-    J.tiles_c[i] = cdiv(d[i].cols, 256);
-    J.start[i + 1] = J.start[i] + cdiv(d[i].rows, 64) * J.tiles_c[i];
-  }
-  if (J.start[n] == 0) return hipSuccess;
+  if (make_transpose_jobs(d, n, J) == 0) return hipSuccess;
   hipLaunchKernelGGL(transpose_bf16_k, dim3(J.start[n]), dim3(256), 0, s, J);
   return hipGetLastError();
 }

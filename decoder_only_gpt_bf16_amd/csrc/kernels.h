@@ -107,6 +107,62 @@ struct TransposeDesc {
   int rows, cols;
 };
 hipError_t launch_transpose(const TransposeDesc* d, int n, hipStream_t s);
+
+// The same jobs as a kernel argument: blocks [start[j], start[j + 1]) of a
+// launch cover matrix j in 64-row x 256-column tiles.  A thread moves one
+// 8 x 8 block: 8 row vectors of 16 bytes in, transposed in registers (halves
+// of 32-bit words regrouped), 8 row vectors of the transpose out.  A wave
+// covers 64 x 64 elements as 8 x 8 such blocks, so that both its loads and
+// its stores are whole 128-byte rows of 8 lanes.  256 threads per block.
+struct TransposeJobs {
+  const bf16* src[TRANSPOSE_MAX];
+  bf16* dst[TRANSPOSE_MAX];
+  int rows[TRANSPOSE_MAX], cols[TRANSPOSE_MAX], tiles_c[TRANSPOSE_MAX];
+  int start[TRANSPOSE_MAX + 1];
+  int n;
+};
+// fills J from d[0 .. n); returns the number of blocks the jobs need
+inline int make_transpose_jobs(const TransposeDesc* d, int n, TransposeJobs& J) {
+  J.n = n;
+  J.start[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    J.src[i] = static_cast<const bf16*>(d[i].src);
+    J.dst[i] = static_cast<bf16*>(d[i].dst);
+    J.rows[i] = d[i].rows;
+    J.cols[i] = d[i].cols;
+    J.tiles_c[i] = (d[i].cols + 255) / 256;
+    J.start[i + 1] = J.start[i] + (d[i].rows + 63) / 64 * J.tiles_c[i];
+  }
+  return J.start[n];
+}
+// block `bid` (< the count above) of the jobs
+__device__ __forceinline__ void transpose_block(const TransposeJobs& J, int bid) {
+  int j = 0;
+  while (j + 1 < J.n && bid >= J.start[j + 1]) ++j;
+  const int tid = bid - J.start[j];
+  const int R = J.rows[j], Cc = J.cols[j];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = (tid / J.tiles_c[j]) * 64 + 8 * (lane >> 3);
+  const int c = (tid % J.tiles_c[j]) * 256 + 64 * wave + 8 * (lane & 7);
+  if (r >= R || c >= Cc) return;
+  const bf16* src = J.src[j] + (long)r * Cc + c;
+  uint4 in[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const uint4*>(src + (long)i * Cc);
+  bf16* dst = J.dst[j] + (long)c * R + r;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    // output row q (source column q): word k pairs source rows 2k and 2k + 1
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * k])[q >> 1];
+      const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * k + 1])[q >> 1];
+      w[k] = (q & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<uint4*>(dst + (long)q * R) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
 hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -153,8 +209,11 @@ hipError_t launch_qk_bwd(int dtype, int B, int T, int H, int D, int rope, int qk
 // qk_norm != 0 promises RMS-normalised q and k (|q|, |k| <= sqrt(D)), which
 // lets the softmax use a fixed shift instead of a running maximum.
 // window > 0: query i attends to keys i - window + 1 .. i only (0: full causal).
+// side[0 .. nside): bf16 transposes that ride in the same launch (MFMA path:
+// extra blocks after the attention's; other paths: a launch of their own
+// after it), nside <= TRANSPOSE_MAX.
 hipError_t launch_attn_fwd(int dtype, int B, int T, int H, int D, int qk_norm, int window, const void* qkv, void* o,
-                           float* lse, hipStream_t s);
+                           float* lse, const TransposeDesc* side, int nside, hipStream_t s);
 // delta[b, h, t] = sum_d dO * O (fp32 [B, H, T]).
 hipError_t launch_attn_delta(int dtype, int B, int T, int H, int D, const void* o, const void* dO,
                              float* delta, hipStream_t s);

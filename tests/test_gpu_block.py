@@ -32,13 +32,17 @@ CASES = [
     ("gpt2_block", dict(B=2, T=200, window=64), True),
     ("tiny_gpt_fp32", dict(B=2, T=32, window=5), False),
     ("d20_block", dict(window=512), False),
+    # bf16 with head_dim 32: the vector-ALU attention, with the transposed
+    # weights of the backward written by a launch of their own
+    ("gpt2_block", dict(B=2, T=130, n_head=24), True),
 ]
 
 
 def _ids(c):
     name, sz, aff = c
     win = f"-W{sz['window']}" if "window" in sz else ""
-    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{win}{'-affine' if aff else ''}"
+    heads = f"-H{sz['n_head']}" if "n_head" in sz else ""
+    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{win}{heads}{'-affine' if aff else ''}"
 
 
 def _run(w, random_affine, seed=0):
