@@ -937,8 +937,16 @@ Plan plan_mfma(const GemmDesc& d) {
   // whole rounds of the 256 CUs: 256 x 320 when it fills them exactly and
   // 256 x 256 would leave a partial round (e.g. N = 5120, M = 8192)
   const bool r320 = d.N % 320 == 0 && t320 >= 256 && t320 % 256 == 0 && t256 % 256 != 0;
+  // 256 x 192 (k-contiguous bf16 operands, store and GELU epilogues) where
+  // it fills the CUs in whole rounds and 256 x 256 would not: the GPT-2
+  // width's N = 3072 at M = 8192 and N = 768 at M = 16384 (a 128 x 192 tile
+  // for N = 768 at M = 8192 measured no faster than 128 x 128)
+  const bool r192 = d.N % 192 == 0 && !d.a_kmaj && !d.b_kmaj && !d.f8_sa &&
+                    (d.epi == EPI_STORE || d.epi == EPI_GELU) && (long)cdiv(d.M, 256) * (d.N / 192) % 256 == 0 &&
+                    t256 % 256 != 0;
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
   else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
+  else if (r192) { pl.BMv = 256; pl.BNv = 192; }
   else if (t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else if (d.N % 160 == 0 && t160 >= 240 && t160 % 256 <= 16) { pl.BMv = 256; pl.BNv = 160; }
   else { pl.BMv = 128; pl.BNv = 128; }
@@ -986,6 +994,16 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
       hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 320, 8, 4, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
+    }
+  }
+  if (pl.BNv == 192) {
+    // 8 waves of 64 x 96
+    if constexpr (F8 == 0 && !AK && !BKm && (EPI == EPI_STORE || EPI == EPI_GELU)) {
+      dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 192, 8, 4, F8>), grid, dim3(512), 0, s, p);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
     }
   }
   if (pl.BNv == 160) {
