@@ -216,7 +216,11 @@ Fp8FwdWs fp8_fwd_layout(const Dims& d, Arena& a) {
 
 struct BwdWs {
   void *du, *da, *dx1, *dO, *dqkv;
-  float *delta, *colpart, *colsum, *split;
+  float *delta, *split;
+  // column partials, each reduction its own so that one launch at the end
+  // finishes them all: the two LayerNorms' gain and bias [2][nblk][C], the
+  // biases of proj, fc, out and qkv [colsum_part_blocks(N)][width]
+  float *colpart1, *colpart2, *bpart[4];
   // FP8: codes of the current gradient [N][Out] and their transpose
   // [Out][Np], amax partials, the gradients' scales [4][4]
   uint8_t *qg, *qgT;
@@ -308,8 +312,14 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   w.dO = a.take(N * C * es);
   w.dqkv = a.take(N * 3 * C * es);
   w.delta = a.take_n<float>((size_t)d.B * d.H * d.T);
-  w.colpart = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
-  w.colsum = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, 4 * C)));
+  if (cfg->norm == GPT_NORM_LAYERNORM) {
+    w.colpart1 = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
+    w.colpart2 = a.take_n<float>(2 * (size_t)norm_bwd_blocks(d.N) * C);
+  }
+  if (cfg->bias) {
+    const int widths[4] = {(int)C, 4 * (int)C, (int)C, 3 * (int)C};
+    for (int i = 0; i < 4; ++i) w.bpart[i] = static_cast<float*>(a.take(colsum_scratch_bytes(d.N, widths[i])));
+  }
   w.split = static_cast<float*>(a.take(split_need(d, cfg)));
   if (cfg->fp8) {
     w.qg = a.take_n<uint8_t>(N * 4 * C);
@@ -657,7 +667,15 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
   }
-  if (cfg->bias) RUN("proj_bias", launch_colsum(ty, N, C, C, dy, gr->b_proj, accumulate, b.colsum, s));
+  // column sums (bias and LayerNorm gradients): partials as their inputs
+  // appear, one launch at the end reduces them all
+  ColsumJob cj[COLSUM_JOBS_MAX];
+  int ncj = 0;
+  const int pb = colsum_part_blocks(N);
+  if (cfg->bias) {
+    RUN("proj_bias", launch_colsum_part(ty, N, C, C, dy, b.bpart[0], s));
+    cj[ncj++] = {b.bpart[0], pb, C, gr->b_proj};
+  }
   g = wt ? lin_dgrad_t(d, b.du, 4 * C, sv.wt_fc, C, EPI_STORE) : lin_dgrad(d, b.du, 4 * C, w->w_fc, C, EPI_STORE);
   g.out = b.da; g.ldc = C;
   if (f8) {
@@ -668,12 +686,15 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
   }
-  if (cfg->bias) RUN("fc_bias", launch_colsum(ty, N, 4 * C, 4 * C, b.du, gr->b_fc, accumulate, b.colsum, s));
+  if (cfg->bias) {
+    RUN("fc_bias", launch_colsum_part(ty, N, 4 * C, 4 * C, b.du, b.bpart[1], s));
+    cj[ncj++] = {b.bpart[1], pb, 4 * C, gr->b_fc};
+  }
   // norm 2 backward + residual
-  RUN("norm2_bwd", launch_norm_bwd(ty, kind, N, C, sv.x1, w->ln2_w, b.da, dy, cfg->norm_eps, b.dx1, b.colpart, ln, s));
+  RUN("norm2_bwd", launch_norm_bwd(ty, kind, N, C, sv.x1, w->ln2_w, b.da, dy, cfg->norm_eps, b.dx1, b.colpart2, ln, s));
   if (ln) {
-    RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln2_w, accumulate, s));
-    if (cfg->bias) RUN("norm2_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln2_b, accumulate, s));
+    cj[ncj++] = {b.colpart2, nblk, C, gr->ln2_w};
+    if (cfg->bias) cj[ncj++] = {b.colpart2 + (size_t)nblk * C, nblk, C, gr->ln2_b};
   }
   // attention output projection
   g = wt ? lin_dgrad_t(d, b.dx1, C, sv.wt_o, C, EPI_STORE) : lin_dgrad(d, b.dx1, C, w->w_o, C, EPI_STORE);
@@ -686,7 +707,10 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
   }
-  if (cfg->bias) RUN("out_bias", launch_colsum(ty, N, C, C, b.dx1, gr->b_o, accumulate, b.colsum, s));
+  if (cfg->bias) {
+    RUN("out_bias", launch_colsum_part(ty, N, C, C, b.dx1, b.bpart[2], s));
+    cj[ncj++] = {b.bpart[2], pb, C, gr->b_o};
+  }
   // attention
   const QkBwd qk{cfg->rope, cfg->qk_norm, N, sv.cs, sv.qkr};
   if (attn_mfma_supported(ty, d.D)) {
@@ -716,14 +740,18 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);
   }
-  if (cfg->bias) RUN("qkv_bias", launch_colsum(ty, N, 3 * C, 3 * C, b.dqkv, gr->b_qkv, accumulate, b.colsum, s));
+  if (cfg->bias) {
+    RUN("qkv_bias", launch_colsum_part(ty, N, 3 * C, 3 * C, b.dqkv, b.bpart[3], s));
+    cj[ncj++] = {b.bpart[3], pb, 3 * C, gr->b_qkv};
+  }
   // norm 1 backward + residual
-  RUN("norm1_bwd", launch_norm_bwd(ty, kind, N, C, x, w->ln1_w, b.da, b.dx1, cfg->norm_eps, dx, b.colpart, ln, s));
+  RUN("norm1_bwd", launch_norm_bwd(ty, kind, N, C, x, w->ln1_w, b.da, b.dx1, cfg->norm_eps, dx, b.colpart1, ln, s));
   if (ln) {
-    RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart, gr->ln1_w, accumulate, s));
-    if (cfg->bias) RUN("norm1_cols", launch_colsum_finish(C, nblk, b.colpart + (size_t)nblk * C, gr->ln1_b, accumulate, s));
+    cj[ncj++] = {b.colpart1, nblk, C, gr->ln1_w};
+    if (cfg->bias) cj[ncj++] = {b.colpart1 + (size_t)nblk * C, nblk, C, gr->ln1_b};
   }
   if (nwg) RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, split_need(d, cfg), s));
+  if (ncj) RUN("col_sums", launch_colsum_finish_jobs(cj, ncj, accumulate, s));
   return GPT_OK;
 }
 

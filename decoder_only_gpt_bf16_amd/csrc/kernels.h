@@ -180,10 +180,21 @@ hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, con
 int norm_bwd_blocks(int N);
 hipError_t launch_colsum_finish(int C, int nblk, const float* part, float* out, int accumulate,
                                 hipStream_t s);
-// Column sums of a [N, C] matrix (storage dtype) into out fp32 [C] (bias gradients).
+// Several such reductions in one launch: out_j[c] (+)= sum over b < nblk_j of
+// part_j[b][c], each in the same fixed order as launch_colsum_finish.
+constexpr int COLSUM_JOBS_MAX = 8;
+struct ColsumJob {
+  const float* part;
+  int nblk, C;
+  float* out;
+};
+hipError_t launch_colsum_finish_jobs(const ColsumJob* jobs, int n, int accumulate, hipStream_t s);
+// Per-block column partials of a [N, C] matrix (storage dtype, leading
+// dimension ld) for the finish above (bias gradients): part
+// [colsum_part_blocks(N)][C] fp32.
+int colsum_part_blocks(int N);
 size_t colsum_scratch_bytes(int N, int C);
-hipError_t launch_colsum(int dtype, int N, int C, long ld, const void* x, float* out,
-                         int accumulate, float* scratch, hipStream_t s);
+hipError_t launch_colsum_part(int dtype, int N, int C, long ld, const void* x, float* part, hipStream_t s);
 
 // ids outside [0, V) give a zero token embedding (no out-of-range read).
 hipError_t launch_embed_fwd(int dtype, int B, int T, int C, int V, const int32_t* ids, const void* wte,

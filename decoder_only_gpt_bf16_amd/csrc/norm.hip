@@ -190,10 +190,20 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
 // partials in order, their loads issued CF_U at a time, and the runs' sums
 // are then added in run order: a fixed order for any launch.
 constexpr int CF_COLS = 16, CF_SEGS = 16, CF_U = 16;
-__global__ __launch_bounds__(CF_COLS * CF_SEGS) void colsum_finish_k(int C, int nblk, const float* __restrict__ part,
-                                                                     float* __restrict__ out, int accumulate) {
+// jobs of one launch: blocks [start[j], start[j + 1]) take job j
+struct ColsumJobs {
+  ColsumJob job[COLSUM_JOBS_MAX];
+  int start[COLSUM_JOBS_MAX + 1];
+  int n;
+};
+__global__ __launch_bounds__(CF_COLS * CF_SEGS) void colsum_finish_k(ColsumJobs J, int accumulate) {
+  int j = 0;
+  while (j + 1 < J.n && (int)blockIdx.x >= J.start[j + 1]) ++j;
+  const int C = J.job[j].C, nblk = J.job[j].nblk;
+  const float* __restrict__ part = J.job[j].part;
+  float* __restrict__ out = J.job[j].out;
   const int lc = threadIdx.x % CF_COLS, seg = threadIdx.x / CF_COLS;
-  const int c = blockIdx.x * CF_COLS + lc;
+  const int c = (blockIdx.x - J.start[j]) * CF_COLS + lc;
   const int per = (nblk + CF_SEGS - 1) / CF_SEGS;
   const int b1 = min(nblk, (seg + 1) * per);
   float s = 0.0f;
@@ -283,30 +293,38 @@ hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, con
   return hipGetLastError();
 }
 
+hipError_t launch_colsum_finish_jobs(const ColsumJob* jobs, int n, int accumulate, hipStream_t s) {
+  if (n < 0 || n > COLSUM_JOBS_MAX) return hipErrorInvalidValue;
+  ColsumJobs J{};
+  J.n = n;
+  J.start[0] = 0;
+  for (int j = 0; j < n; ++j) {
+    J.job[j] = jobs[j];
+    J.start[j + 1] = J.start[j] + cdiv(jobs[j].C, CF_COLS);
+  }
+  if (J.start[n] == 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_finish_k, dim3(J.start[n]), dim3(CF_COLS * CF_SEGS), 0, s, J, accumulate);
+  return hipGetLastError();
+}
+
 hipError_t launch_colsum_finish(int C, int nblk, const float* part, float* out, int accumulate,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(colsum_finish_k, dim3(cdiv(C, CF_COLS)), dim3(CF_COLS * CF_SEGS), 0, s, C, nblk, part, out,
-                     accumulate);
-  return hipGetLastError();
+  const ColsumJob job{part, nblk, C, out};
+  return launch_colsum_finish_jobs(&job, 1, accumulate, s);
 }
 
 size_t colsum_scratch_bytes(int N, int C) {
   return align256((size_t)cdiv(N, COLSUM_ROWS) * C * sizeof(float));
 }
 
-hipError_t launch_colsum(int dtype, int N, int C, long ld, const void* x, float* out, int accumulate,
-                         float* scratch, hipStream_t s) {
-  if (N <= 0) {
-    if (!accumulate) return hipMemsetAsync(out, 0, C * sizeof(float), s);
-    return hipSuccess;
-  }
-  const int nblk = cdiv(N, COLSUM_ROWS);
-  dim3 grid(cdiv(C, 256), nblk);
+int colsum_part_blocks(int N) { return std::max(1, cdiv(N, COLSUM_ROWS)); }
+
+hipError_t launch_colsum_part(int dtype, int N, int C, long ld, const void* x, float* part, hipStream_t s) {
+  if (N <= 0 || C <= 0) return hipErrorInvalidValue;
+  dim3 grid(cdiv(C, 256), colsum_part_blocks(N));
   if (dtype == 1)
-    hipLaunchKernelGGL(colsum_part_k<bf16>, grid, dim3(256), 0, s, N, C, ld, (const bf16*)x, scratch, COLSUM_ROWS);
+    hipLaunchKernelGGL(colsum_part_k<bf16>, grid, dim3(256), 0, s, N, C, ld, (const bf16*)x, part, COLSUM_ROWS);
   else
-    hipLaunchKernelGGL(colsum_part_k<float>, grid, dim3(256), 0, s, N, C, ld, (const float*)x, scratch, COLSUM_ROWS);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_colsum_finish(C, nblk, scratch, out, accumulate, s);
+    hipLaunchKernelGGL(colsum_part_k<float>, grid, dim3(256), 0, s, N, C, ld, (const float*)x, part, COLSUM_ROWS);
+  return hipGetLastError();
 }
