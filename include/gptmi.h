@@ -18,7 +18,9 @@
  *    caller allocates and owns every buffer (weights, activations, saved
  *    activations, workspace, gradients).  The library never allocates or
  *    frees device memory, never synchronises the stream, and keeps no state
- *    between calls apart from a thread-local error message.
+ *    between calls apart from a thread-local error message, the opt-in
+ *    trace hooks' event pool (gpt_trace_begin) and the fixed device scratch
+ *    of gpt_adamw_step_noalloc (documented with it).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every kernel of a call is enqueued on it in order.
  *  - Activations are row-major [N, C] with N = B*T tokens, row n = b*T + t.
@@ -127,8 +129,9 @@ size_t gpt_workspace_bytes(const gpt_config* cfg, int B, int T);
  *         matching gpt_block_bwd.
  *   y     [B*T, C] output (dtype).
  *   saved gpt_block_saved_bytes() bytes, filled for the backward (with the
- *         RoPE table it reads too); NULL runs inference only (intermediates
- *         then live in the workspace).
+ *         RoPE table and, in bf16 without fp8, transposed copies of W_fc,
+ *         W_o and W_qkv that it reads too); NULL runs inference only
+ *         (intermediates then live in the workspace).
  *   ws    gpt_workspace_bytes() bytes of temporaries: the FP8 codes with
  *         cfg->fp8, the intermediates when saved is NULL.  Where neither
  *         applies the forward does not touch it and NULL is accepted.
@@ -145,8 +148,9 @@ int gpt_block_fwd(const gpt_config* cfg, int B, int T, const void* x,
 
 /* Backward of gpt_block_fwd.  dy [B*T, C] upstream gradient (dtype);
  * dx [B*T, C] output gradient (dtype); parameter gradients into g (fp32,
- * overwritten or accumulated per `accumulate`).  `saved` and `x` must be
- * those of the matching forward.  Same errors as gpt_block_fwd. */
+ * overwritten or accumulated per `accumulate`).  `saved`, `x` and the
+ * weights `w` must be those of the matching forward (the input gradients
+ * read the forward's transposed weights from `saved`).  Same errors as gpt_block_fwd. */
 int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x,
                   const void* dy, const gpt_block_weights* w,
                   const void* saved, void* dx, const gpt_block_grads* g,
