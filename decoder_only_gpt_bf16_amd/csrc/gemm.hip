@@ -335,6 +335,27 @@ struct Stage8 {
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// all but this wave's n most recent copies have landed (vector-memory loads
+// retire in issue order); n is wave-uniform, at most 15
+__device__ __forceinline__ void wait_loads_but(int n) {
+  switch (n) {
+#define WB(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    WB(1) WB(2) WB(3) WB(4) WB(5) WB(6) WB(7) WB(8) WB(9) WB(10) WB(11) WB(12) WB(13) WB(14) WB(15)
+#undef WB
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+// copy instructions wave w issues for an R-row operand staged by NT threads
+// (R * 8 16-byte units; the last instruction is issued only by the waves it
+// reaches, as in the staging structs)
+template <int R, int NT>
+__device__ __forceinline__ int copies_of_wave(int w) {
+  constexpr int NL = (R * 8 + NT - 1) / NT;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) c += (NT / 64 * i + w < R * 8 / 64) ? 1 : 0;
+  return c;
+}
 
 template <int TM, int TN>
 struct Frags {
@@ -373,7 +394,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   // the whole tile, double-buffered, with rows padded to QKP floats
   constexpr int QKP = 260;
   constexpr int QK_UNITS = EPI == EPI_QKNORM ? 2 * 64 * QKP / 4 : 0;
-  constexpr int LDS_UNITS0 = 2 * STAGE_UNITS > EPI_UNITS ? 2 * STAGE_UNITS : EPI_UNITS;
+  // 256 x 160 bf16 tiles keep three k-tile stages (156 KB), so that two
+  // tiles' copies are in flight while the MFMAs run; the others keep two
+  constexpr bool PIPE3 = F8 == 0 && NW == 8 && BM == 256 && BN == 160;
+  constexpr int NSTAGE = PIPE3 ? 3 : 2;
+  constexpr int LDS_UNITS0 = NSTAGE * STAGE_UNITS > EPI_UNITS ? NSTAGE * STAGE_UNITS : EPI_UNITS;
   __shared__ uint4 lds[LDS_UNITS0 > QK_UNITS ? LDS_UNITS0 : QK_UNITS];
   using SA = Stage<A_KMAJ, BM, NT>;
   using SB = Stage<B_KMAJ, BN, NT>;
@@ -459,6 +484,84 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][i][r] *= inv;
+  } else if constexpr (PIPE3) {
+    static_assert(TM * TN <= 8, "fragment pipeline");
+    // Tile t + 2's copies go into the stage tile t - 1 used, as tile t
+    // starts; at the end of tile t every wave waits only for tile t + 1
+    // (tile t + 2's copies stay in flight).  Unrolled by three so that every
+    // stage index is a compile-time constant.
+    const int ncp = __builtin_amdgcn_readfirstlane(copies_of_wave<BM, NT>(wave) + copies_of_wave<BN, NT>(wave));
+    auto issue_s = [&](int t, auto sc) __attribute__((always_inline)) {
+      uint4* st = lds + decltype(sc)::value * STAGE_UNITS;
+      const int k0 = kbeg + t * BK;
+      SA::direct(st, ra, p.lda, m0, p.M, k0, kend);
+      SB::direct(st + SA_UNITS, rb, p.ldb, n0, p.N, k0, kend);
+    };
+    auto read_s = [&](Frags<TM, TN>& Fr, auto sc, int kk) __attribute__((always_inline)) {
+      const uint4* As = lds + decltype(sc)::value * STAGE_UNITS;
+      const uint4* Bs = As + SA_UNITS;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) Fr.a[i] = SA::frag(As, wm + 32 * i + lrow, kk, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Fr.b[j] = SB::frag(Bs, wn + 32 * j + lrow, kk, lane);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    if (nk > 0) {
+      issue_s(0, S0{});
+      if (nk > 1) issue_s(1, S1{});
+      wait_loads_but(nk > 1 ? ncp : 0);
+      block_barrier();
+      read_s(F[0], S0{}, 0);
+    }
+    auto ktile = [&](int t, auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      using SN = std::integral_constant<int, (S + 1) % 3>;
+      using SI = std::integral_constant<int, (S + 2) % 3>;
+      const bool more2 = t + 2 < nk;
+      if (more2) issue_s(t + 2, SI{});
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        Frags<TM, TN>& cur = F[kk & 1];
+        Frags<TM, TN>& nxt = F[(kk + 1) & 1];
+        constexpr int NMF = TM * TN;
+        constexpr int FIRST = NMF / 2;
+        if (kk + 1 < KK) {
+          read_s(nxt, sc, kk + 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < NMF; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int q = 0; q < FIRST; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          // tile t + 1 has landed and every wave is done with stage S (after
+          // the last tile this reads a stale stage that is never used)
+          wait_loads_but(more2 ? ncp : 0);
+          wait_lds();
+          block_barrier();
+          read_s(nxt, SN{}, 0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = FIRST; q < NMF; ++q)
+            acc[q / TM][q % TM] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    for (int t = 0; t < nk; t += 3) {
+      ktile(t, S0{});
+      if (t + 1 < nk) ktile(t + 1, S1{});
+      if (t + 2 < nk) ktile(t + 2, S2{});
+    }
   } else if constexpr (PIPE) {
     if (nk > 0) {
       issue(0);
