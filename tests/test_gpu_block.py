@@ -35,6 +35,10 @@ CASES = [
     # bf16 with head_dim 32: the vector-ALU attention, with the transposed
     # weights of the backward written by a launch of their own
     ("gpt2_block", dict(B=2, T=130, n_head=24), True),
+    # the d20 form at C = 640 over 16384 tokens: the 256 x 160 GEMM tiles with
+    # k-tile counts 10, 30 and 40 (all three remainders of the loop's
+    # unrolling by three)
+    ("d20_block", dict(B=8, T=2048, n_embd=640, n_head=5), False),
 ]
 
 
@@ -42,7 +46,8 @@ def _ids(c):
     name, sz, aff = c
     win = f"-W{sz['window']}" if "window" in sz else ""
     heads = f"-H{sz['n_head']}" if "n_head" in sz else ""
-    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{win}{heads}{'-affine' if aff else ''}"
+    width = f"-C{sz['n_embd']}" if "n_embd" in sz else ""
+    return f"{name}-B{sz.get('B', 'full')}-T{sz.get('T', 'full')}{win}{heads}{width}{'-affine' if aff else ''}"
 
 
 def _run(w, random_affine, seed=0):
