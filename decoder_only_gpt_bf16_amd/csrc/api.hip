@@ -221,9 +221,10 @@ struct BwdWs {
   // finishes them all: the two LayerNorms' gain and bias [2][nblk][C], the
   // biases of proj, fc, out and qkv [colsum_part_blocks(N)][width]
   float *colpart1, *colpart2, *bpart[4];
-  // FP8: codes of the current gradient [N][Out] and their transpose
-  // [Out][Np], amax partials, the gradients' scales [4][4]
-  uint8_t *qg, *qgT;
+  // FP8: codes of the current gradient [N][Out]; each gradient's transposed
+  // codes [Out][Np] (dy, du, dx1, dqkv), kept for the grouped weight
+  // gradients at the end; amax partials, the gradients' scales [4][4]
+  uint8_t *qg, *qgT[4];
   float *f8part, *f8sc;
 };
 
@@ -293,12 +294,13 @@ size_t split_need(const Dims& d, const gpt_config* cfg) {
   block_wgrads(d, wg);
   size_t need = gemm_group_scratch_bytes(wg, 4, d.dtype);
   if (cfg->fp8) {
+    // the grouped FP8 weight gradients, in the backward's order
     const int C = d.C;
     const GemmDesc f[4] = {fp8_wgrad(d, nullptr, C, nullptr, 4 * C, nullptr, 0),
                            fp8_wgrad(d, nullptr, 4 * C, nullptr, C, nullptr, 0),
                            fp8_wgrad(d, nullptr, C, nullptr, C, nullptr, 0),
                            fp8_wgrad(d, nullptr, 3 * C, nullptr, C, nullptr, 0)};
-    for (const GemmDesc& g : f) need = std::max(need, gemm_fp8_split_scratch_bytes(g));
+    need = std::max(need, gemm_group_fp8_scratch_bytes(f, 4));
   }
   return need;
 }
@@ -323,7 +325,8 @@ BwdWs bwd_layout(const Dims& d, const gpt_config* cfg, Arena& a) {
   w.split = static_cast<float*>(a.take(split_need(d, cfg)));
   if (cfg->fp8) {
     w.qg = a.take_n<uint8_t>(N * 4 * C);
-    w.qgT = a.take_n<uint8_t>(4 * C * fp8_np(N));
+    const size_t outs[4] = {C, 4 * C, C, 3 * C};
+    for (int i = 0; i < 4; ++i) w.qgT[i] = a.take_n<uint8_t>(outs[i] * fp8_np(N));
     w.f8part = a.take_n<float>(fp8_q2d_parts(1));
     w.f8sc = a.take_n<float>(16);
   }
@@ -618,13 +621,14 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   const bool ln = kind == GPT_NORM_LAYERNORM;
 
   // FP8 (cfg->fp8): each incoming gradient is quantized once (E5M2) into
-  // codes for its input-gradient GEMM and transposed codes for its weight-
-  // gradient GEMM, which runs right away (the code buffers serve the next
-  // layer); the weights' and activations' codes come from the forward.
-  // Gradient scale slots in b.f8sc: 0 dy, 1 du, 2 dx1, 3 dqkv.
+  // codes for its input-gradient GEMM (the buffer serves the next layer)
+  // and transposed codes of its own for the weight gradients, which run as
+  // one grouped launch at the end as in bf16; the weights' and activations'
+  // codes come from the forward.  Gradient slots (scales in b.f8sc,
+  // transposed codes in b.qgT): 0 dy, 1 du, 2 dx1, 3 dqkv.
   const bool f8 = cfg->fp8 != 0;
   auto fp8_grad = [&](const void* dY, int Out, int slot) -> int {
-    const Fp8Q2d qg = {dY, b.qg, b.qgT, fp8_np(N), N, Out, b.f8sc + 4 * slot};
+    const Fp8Q2d qg = {dY, b.qg, b.qgT[slot], fp8_np(N), N, Out, b.f8sc + 4 * slot};
     RUN("fp8_quant_g", launch_fp8_quantize_2d(&qg, 1, FP8_E5M2, b.f8part, s));
     return GPT_OK;
   };
@@ -638,12 +642,14 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     RUN(name, launch_gemm_fp8(g, 2, nullptr, s));
     return GPT_OK;
   };
-  // dW[Out][In] (+)= q(dY)^T q(X): the gradient's and the activation's transposed codes
-  auto fp8_wg = [&](const char* name, int Out, const uint8_t* qxT, int In, float* dW, int gslot, int xslot) -> int {
-    GemmDesc g = fp8_wgrad(d, b.qgT, Out, qxT, In, dW, accumulate);
+  // dW[Out][In] (+)= q(dY)^T q(X): the gradient's and the activation's
+  // transposed codes, gathered for the grouped launch at the end
+  GemmDesc wg8[GEMM_GROUP_MAX];
+  int nwg8 = 0;
+  auto fp8_wg = [&](int Out, const uint8_t* qxT, int In, float* dW, int gslot, int xslot) {
+    GemmDesc g = fp8_wgrad(d, b.qgT[gslot], Out, qxT, In, dW, accumulate);
     g.f8_sa = b.f8sc + 4 * gslot; g.f8_sb = sv.f8sc + 4 * xslot;
-    RUN(name, launch_gemm_fp8(g, 2, b.split, s));
-    return GPT_OK;
+    wg8[nwg8++] = g;
   };
 
   // bf16: the input gradients through W_fc, W_o and W_qkv read the
@@ -651,9 +657,9 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   // sides of those GEMMs); W_proj's is read as it lies (its wide tiles run
   // as fast either way)
   const bool wt = keeps_wt(d, cfg);
-  // weight gradients depend on nothing computed later: in bf16 they are
-  // gathered and run as one grouped launch at the end of the backward (one
-  // launch fills the machine where each alone would leave CUs idle)
+  // weight gradients depend on nothing computed later: they are gathered
+  // and run as one grouped launch at the end of the backward (one launch
+  // fills the machine where each alone would leave CUs idle)
   GemmDesc wg[GEMM_GROUP_MAX];
   int nwg = 0;
   // MLP: y = x1 + gelu(a2 W_fc^T + b_fc) W_proj^T + b_proj
@@ -662,7 +668,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   if (f8) {
     if ((st = fp8_grad(dy, C, 0))) return st;
     if ((st = fp8_dgrad("proj_dgrad_gelu", g, C, sv.qWprojT, 4 * C, 0, 7))) return st;
-    if ((st = fp8_wg("proj_wgrad", C, sv.qgT, 4 * C, gr->w_proj, 0, 6))) return st;
+    fp8_wg(C, sv.qgT, 4 * C, gr->w_proj, 0, 6);
   } else {
     RUN("proj_dgrad_gelu", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, dy, C, sv.g, 4 * C, gr->w_proj, accumulate);
@@ -681,7 +687,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   if (f8) {
     if ((st = fp8_grad(b.du, 4 * C, 1))) return st;
     if ((st = fp8_dgrad("fc_dgrad", g, 4 * C, sv.qWfcT, C, 1, 5))) return st;
-    if ((st = fp8_wg("fc_wgrad", 4 * C, sv.qa2T, C, gr->w_fc, 1, 4))) return st;
+    fp8_wg(4 * C, sv.qa2T, C, gr->w_fc, 1, 4);
   } else {
     RUN("fc_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.du, 4 * C, sv.a2, C, gr->w_fc, accumulate);
@@ -702,7 +708,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   if (f8) {
     if ((st = fp8_grad(b.dx1, C, 2))) return st;
     if ((st = fp8_dgrad("out_dgrad", g, C, sv.qWoT, C, 2, 3))) return st;
-    if ((st = fp8_wg("out_wgrad", C, sv.qoT, C, gr->w_o, 2, 2))) return st;
+    fp8_wg(C, sv.qoT, C, gr->w_o, 2, 2);
   } else {
     RUN("out_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.dx1, C, sv.o, C, gr->w_o, accumulate);
@@ -735,7 +741,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
   if (f8) {
     if ((st = fp8_grad(b.dqkv, 3 * C, 3))) return st;
     if ((st = fp8_dgrad("qkv_dgrad", g, 3 * C, sv.qWqkvT, C, 3, 1))) return st;
-    if ((st = fp8_wg("qkv_wgrad", 3 * C, sv.qa1T, C, gr->w_qkv, 3, 0))) return st;
+    fp8_wg(3 * C, sv.qa1T, C, gr->w_qkv, 3, 0);
   } else {
     RUN("qkv_dgrad", launch_gemm(g, ty, nullptr, s));
     wg[nwg++] = lin_wgrad(d, b.dqkv, 3 * C, sv.a1, C, gr->w_qkv, accumulate);
@@ -751,6 +757,7 @@ int gpt_block_bwd(const gpt_config* cfg, int B, int T, const void* x, const void
     if (cfg->bias) cj[ncj++] = {b.colpart1 + (size_t)nblk * C, nblk, C, gr->ln1_b};
   }
   if (nwg) RUN("wgrad_group", launch_gemm_group(wg, nwg, ty, b.split, split_need(d, cfg), s));
+  if (nwg8) RUN("wgrad_group", launch_gemm_group_fp8(wg8, nwg8, b.split, split_need(d, cfg), s));
   if (ncj) RUN("col_sums", launch_colsum_finish_jobs(cj, ncj, accumulate, s));
   return GPT_OK;
 }

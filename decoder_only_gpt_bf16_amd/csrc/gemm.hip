@@ -878,7 +878,8 @@ struct GemmGroup {
 struct StreamKPlan {
   int G;          // blocks
   int R;          // whole tiles per block
-  int nk;         // k-steps (of BK) per tile
+  int nk;         // k units per tile
+  int ku;         // k elements per unit (one k tile: BK, or 128 for FP8 codes)
   int rem;        // tiles left for the split phase
   int S;          // partial slots per split tile
   float* part;    // [rem][S][BM * BN]
@@ -904,13 +905,13 @@ __device__ __forceinline__ void group_tile(const GemmGroup& g, int tile, int& q,
   tile_coords(g.p[q], tile - g.start[q], g.start[q + 1] - g.start[q], tm, tn);
 }
 
-template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM>
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM, int F8 = 0>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_streamk(GemmGroup g, StreamKPlan k) {
   const int b = blockIdx.x;
   int q, tm, tn;
   for (int r = 0; r < k.R; ++r) {
     group_tile<BM, BN>(g, r * k.G + b, q, tm, tn);
-    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(g.p[q], tm, tn, 0, g.p[q].K, nullptr);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM, F8>(g.p[q], tm, tn, 0, g.p[q].K, nullptr);
     block_barrier();  // the epilogue's LDS staging is done before the next prologue
   }
   if (k.rem == 0) return;
@@ -926,7 +927,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_streamk(GemmGroup g, StreamKP
       const int first = sk_block_of(k, (long)rt * k.nk);
       part = k.part + ((long)rt * k.S + (b - first)) * (BM * BN);
     }
-    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM>(p, tm, tn, k0 * BK, min(p.K, k1 * BK), part);
+    gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM, F8>(p, tm, tn, k0 * k.ku, min(p.K, k1 * k.ku), part);
     block_barrier();
     u += k1 - k0;
   }
@@ -1326,18 +1327,29 @@ hipError_t launch_gemm_fp8(const GemmDesc& d, int mode, void* ws, hipStream_t s)
 // problems do not qualify (bf16 MFMA operands, both k-major, fp32 output,
 // one K that is a multiple of BK).
 constexpr int SK_BLOCKS = 256;
-static bool streamk_plan(const GemmDesc* d, int n, int dtype, GemmGroup& g, StreamKPlan& k, size_t& scratch) {
+// fp8: FP8 codes (dY in E5M2 times X in E4M3, both with k = tokens
+// contiguous, launch_gemm_fp8's operand rules), in 128-element k units;
+// otherwise bf16 with both operands k-major, in BK-element units
+static bool streamk_plan(const GemmDesc* d, int n, int dtype, bool fp8, GemmGroup& g, StreamKPlan& k,
+                         size_t& scratch) {
   if (n <= 0 || n > GEMM_GROUP_MAX || dtype != 1) return false;
   const int K = d[0].K;
-  if (K <= 0 || K % BK) return false;
+  if (K <= 0 || K % (fp8 ? 16 : BK)) return false;
   g = GemmGroup{};
   g.count = n;
   int total = 0;
   for (int i = 0; i < n; ++i) {
     uint32_t ab = 0, bb = 0;
-    if (d[i].epi != EPI_F32 || !d[i].a_kmaj || !d[i].b_kmaj || d[i].K != K || d[i].M <= 0 || d[i].N <= 0 ||
-        !mfma_ok(d[i], ab, bb))
+    if (d[i].epi != EPI_F32 || d[i].K != K || d[i].M <= 0 || d[i].N <= 0) return false;
+    if (fp8) {
+      if (d[i].a_kmaj || d[i].b_kmaj || d[i].lda % 16 || d[i].ldb % 16) return false;
+      const long a = (long)(d[i].M - 1) * d[i].lda + K, b = (long)(d[i].N - 1) * d[i].ldb + K;
+      if (a >= (1L << 31) || b >= (1L << 31)) return false;
+      ab = (uint32_t)a;
+      bb = (uint32_t)b;
+    } else if (!d[i].a_kmaj || !d[i].b_kmaj || !mfma_ok(d[i], ab, bb)) {
       return false;
+    }
     GemmParams p = make_params(d[i]);
     p.tiles_m = cdiv(d[i].M, 256);
     p.tiles_n = cdiv(d[i].N, 256);
@@ -1353,7 +1365,8 @@ static bool streamk_plan(const GemmDesc* d, int n, int dtype, GemmGroup& g, Stre
   k.G = SK_BLOCKS;
   k.R = total / k.G;
   k.rem = total % k.G;
-  k.nk = K / BK;
+  k.ku = fp8 ? 128 : BK;
+  k.nk = cdiv(K, k.ku);
   k.S = 1;
   for (int rt = 0; rt < k.rem; ++rt)
     k.S = std::max(k.S, sk_block_of(k, (long)(rt + 1) * k.nk - 1) - sk_block_of(k, (long)rt * k.nk) + 1);
@@ -1365,27 +1378,57 @@ size_t gemm_group_scratch_bytes(const GemmDesc* d, int n, int dtype) {
   GemmGroup g;
   StreamKPlan k;
   size_t need = 0;
-  if (streamk_plan(d, n, dtype, g, k, need)) return need;
+  if (streamk_plan(d, n, dtype, false, g, k, need)) return need;
   size_t m = 0;
   for (int i = 0; i < n; ++i) m = std::max(m, gemm_split_scratch_bytes(d[i], dtype));
   return m;
+}
+
+size_t gemm_group_fp8_scratch_bytes(const GemmDesc* d, int n) {
+  GemmGroup g;
+  StreamKPlan k;
+  size_t need = 0;
+  if (streamk_plan(d, n, 1, true, g, k, need)) return need;
+  size_t m = 0;
+  for (int i = 0; i < n; ++i) m = std::max(m, gemm_fp8_split_scratch_bytes(d[i]));
+  return m;
+}
+
+// the stream-K kernel and, when tiles were split, the fixup
+template <bool AK, bool BKm, int F8>
+static hipError_t run_streamk(const GemmGroup& g, StreamKPlan& k, void* ws, hipStream_t s) {
+  k.part = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gemm_streamk<AK, BKm, EPI_F32, 256, 256, 8, 2, F8>), dim3(k.G), dim3(512), 0, s, g, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || k.rem == 0) return e;
+  hipLaunchKernelGGL((streamk_fixup<256, 256>), dim3(256 * 256 / 1024, k.rem), dim3(256), 0, s, g, k);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   GemmGroup g;
   StreamKPlan k;
   size_t need = 0;
-  if (streamk_plan(d, n, dtype, g, k, need) && (need == 0 || (ws && ws_bytes >= need))) {
-    k.part = static_cast<float*>(ws);
-    hipLaunchKernelGGL((gemm_streamk<true, true, EPI_F32, 256, 256, 8, 2>), dim3(k.G), dim3(512), 0, s, g, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || k.rem == 0) return e;
-    hipLaunchKernelGGL((streamk_fixup<256, 256>), dim3(256 * 256 / 1024, k.rem), dim3(256), 0, s, g, k);
-    return hipGetLastError();
-  }
+  if (streamk_plan(d, n, dtype, false, g, k, need) && (need == 0 || (ws && ws_bytes >= need)))
+    return run_streamk<true, true, 0>(g, k, ws, s);
   // otherwise one launch per problem
   for (int i = 0; i < n; ++i) {
     hipError_t e = launch_gemm(d[i], dtype, ws, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_group_fp8(const GemmDesc* d, int n, void* ws, size_t ws_bytes, hipStream_t s) {
+  for (int i = 0; i < n; ++i)
+    if (!d[i].f8_sa || !d[i].f8_sb) return hipErrorInvalidValue;
+  GemmGroup g;
+  StreamKPlan k;
+  size_t need = 0;
+  if (streamk_plan(d, n, 1, true, g, k, need) && (need == 0 || (ws && ws_bytes >= need)))
+    return run_streamk<false, false, 2>(g, k, ws, s);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = launch_gemm_fp8(d[i], 2, ws, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

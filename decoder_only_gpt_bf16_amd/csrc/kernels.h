@@ -98,6 +98,11 @@ size_t gemm_fp8_split_scratch_bytes(const GemmDesc& d);
 // gemm_group_scratch_bytes() bytes.
 constexpr int GEMM_GROUP_MAX = 4;
 size_t gemm_group_scratch_bytes(const GemmDesc* d, int n, int dtype);
+// The same grouping for FP8 weight gradients: A = dY codes in E5M2, B = X
+// codes in E4M3, both k contiguous (launch_gemm_fp8's operand rules, mode 2);
+// falls back to one launch_gemm_fp8 each.  `ws` must hold
+// gemm_group_fp8_scratch_bytes() bytes.
+size_t gemm_group_fp8_scratch_bytes(const GemmDesc* d, int n);
 // bf16 transposes dst[c][r] = src[r][c] ([rows][cols] row-major in, [cols][rows]
 // out), up to TRANSPOSE_MAX in one launch; rows and cols multiples of 8
 constexpr int TRANSPOSE_MAX = 4;
@@ -164,6 +169,7 @@ __device__ __forceinline__ void transpose_block(const TransposeJobs& J, int bid)
   }
 }
 hipError_t launch_gemm_group(const GemmDesc* d, int n, int dtype, void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_gemm_group_fp8(const GemmDesc* d, int n, void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Norms, embeddings, attention, cross-entropy, reductions.

@@ -200,14 +200,16 @@ def test_block_parity_stale_workspace(name, Bsz, T):
     print(name, Bsz, T, {k: f"{v:.2e}" for k, v in rep.items()})
 
 
-@pytest.mark.parametrize("name,Bsz,T", [("d20_block", 1, 192), ("d20_block", 2, 2048)])
-def test_block_accumulate_streamk(name, Bsz, T):
+@pytest.mark.parametrize("name,Bsz,T,fp8", [("d20_block", 1, 192, False), ("d20_block", 2, 2048, False),
+                                             ("d20_block", 2, 2048, True)])
+def test_block_accumulate_streamk(name, Bsz, T, fp8):
     """accumulate=1 through the grouped stream-K weight gradients (both the
-    whole tiles' epilogue and the fixup of the split tiles): a second
-    identical backward doubles every parameter gradient exactly (the
-    reductions have a fixed order, so the two passes are bitwise equal)."""
-    w = synth.scaled(synth.BY_NAME[name], B=Bsz, T=T)
-    print_case("block-accumulate-streamk", name, Bsz, T)
+    whole tiles' epilogue and the fixup of the split tiles; bf16, or FP8
+    codes with fp8): a second identical backward doubles every parameter
+    gradient exactly (the reductions have a fixed order, so the two passes
+    are bitwise equal)."""
+    w = synth.scaled(synth.BY_NAME[name], B=Bsz, T=T, fp8=fp8)
+    print_case("block-accumulate-streamk", name, Bsz, T, "fp8" if fp8 else "")
     x, dy, p, r = _run(w, False)
     g1 = {k: v.clone() for k, v in r.g.items() if v is not None}
     r.ws.fill_(255)
