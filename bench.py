@@ -36,7 +36,7 @@ SITE_KERNEL = {
     "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 2, 0>"], "gemm"),
     "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4, 0>"], "gemm"),
     "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4, 0>"], "gemm"),
-    "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2>", "streamk_fixup<256, 256>"], "gemm"),
+    "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2, 0>", "streamk_fixup<256, 256>"], "gemm"),
     # rocprofv3 prints the bf16 instances of the norm kernels this way
     "norm1_fwd": (["norm_fwd_k<bool _Accum, int, E, true>"], "norm"),
     "norm2_fwd": (["norm_fwd_k<bool _Accum, int, E, false>"], "norm"),
