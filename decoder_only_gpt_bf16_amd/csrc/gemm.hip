@@ -230,20 +230,23 @@ struct StageKc {
   // copy instructions per thread; when R * 8 units are not a multiple of the
   // thread count, the last one is issued by the first waves only
   static constexpr int NL = (R * 8 + NT - 1) / NT;
-  static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
-                                                int k0, int kend) {
+  // copy instruction i alone
+  static __device__ __forceinline__ void direct1(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                 int k0, int kend, int i) {
     static_assert(R % 8 == 0, "tile rows a multiple of 8");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if ((R * 8) % NT != 0 && NT / 64 * i + w >= R * 8 / 64) return;
+    const int P = (NT / 64 * i + w) * 64 + lane;
+    const int row = P >> 3;
+    const int u = (P & 7) ^ swz128(row);
+    const int gr = r0 + row, kk = k0 + 8 * u;
+    const uint32_t off = (kk + 8 <= kend && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
+    load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
+  }
+  static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                int k0, int kend) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      if ((R * 8) % NT != 0 && NT / 64 * i + w >= R * 8 / 64) break;
-      const int P = (NT / 64 * i + w) * 64 + lane;
-      const int row = P >> 3;
-      const int u = (P & 7) ^ swz128(row);
-      const int gr = r0 + row, kk = k0 + 8 * u;
-      const uint32_t off = (kk + 8 <= kend && gr < rmax) ? (uint32_t)(((long)gr * ld + kk) * 2) : OOB;
-      load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
-    }
+    for (int i = 0; i < NL; ++i) direct1(lds, rs, ld, r0, rmax, k0, kend, i);
   }
   // A/B operand fragment: tile row `row`, k-step kk, lane half hf
   static __device__ __forceinline__ bf16x8 frag(const uint4* lds, int row, int kk, int lane) {
@@ -260,19 +263,21 @@ template <int R, int NT>
 struct StageKm {
   static constexpr int UPR = R / 8;
   static constexpr int NL = (64 * UPR + NT - 1) / NT;  // as in StageKc
+  static __device__ __forceinline__ void direct1(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
+                                                 int k0, int kend, int i) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if ((64 * UPR) % NT != 0 && NT / 64 * i + w >= UPR) return;
+    const int P = (NT / 64 * i + w) * 64 + lane;
+    const int kr = P / UPR;
+    const int c = (P % UPR) ^ swz_km<UPR>(kr);
+    const int gk = k0 + kr, gc = r0 + 8 * c;
+    const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
+    load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
+  }
   static __device__ __forceinline__ void direct(uint4* lds, __amdgpu_buffer_rsrc_t rs, long ld, int r0, int rmax,
                                                 int k0, int kend) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      if ((64 * UPR) % NT != 0 && NT / 64 * i + w >= UPR) break;
-      const int P = (NT / 64 * i + w) * 64 + lane;
-      const int kr = P / UPR;
-      const int c = (P % UPR) ^ swz_km<UPR>(kr);
-      const int gk = k0 + kr, gc = r0 + 8 * c;
-      const uint32_t off = (gk < kend && gc + 8 <= rmax) ? (uint32_t)(((long)gk * ld + gc) * 2) : OOB;
-      load_lds16(rs, lds + (NT / 64 * i + w) * 64, off);
-    }
+    for (int i = 0; i < NL; ++i) direct1(lds, rs, ld, r0, rmax, k0, kend, i);
   }
   static __device__ __forceinline__ i16x4 tr(const uint4* lds, int krow, int col) {
     const bf16* base = reinterpret_cast<const bf16*>(lds);
@@ -497,6 +502,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
       SA::direct(st, ra, p.lda, m0, p.M, k0, kend);
       SB::direct(st + SA_UNITS, rb, p.ldb, n0, p.N, k0, kend);
     };
+    // copy instruction c of a tile (A's first, then B's)
+    constexpr int NCP = SA::NL + SB::NL;
+    auto issue1 = [&](int t, auto sc, int c) __attribute__((always_inline)) {
+      uint4* st = lds + decltype(sc)::value * STAGE_UNITS;
+      const int k0 = kbeg + t * BK;
+      if (c < SA::NL) SA::direct1(st, ra, p.lda, m0, p.M, k0, kend, c);
+      else SB::direct1(st + SA_UNITS, rb, p.ldb, n0, p.N, k0, kend, c - SA::NL);
+    };
     auto read_s = [&](Frags<TM, TN>& Fr, auto sc, int kk) __attribute__((always_inline)) {
       const uint4* As = lds + decltype(sc)::value * STAGE_UNITS;
       const uint4* Bs = As + SA_UNITS;
@@ -520,7 +533,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
       using SN = std::integral_constant<int, (S + 1) % 3>;
       using SI = std::integral_constant<int, (S + 2) % 3>;
       const bool more2 = t + 2 < nk;
-      if (more2) issue_s(t + 2, SI{});
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -532,9 +544,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
           read_s(nxt, sc, kk + 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int q = 0; q < NMF; ++q)
+          for (int q = 0; q < NMF; ++q) {
             acc[q / TM][q % TM] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[q / TM], cur.a[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+            // tile t + 2's copies, one after every other MFMA of the first
+            // KK - 1 steps, so that no wave stalls on a burst of them
+#pragma unroll
+            for (int c = 0; c < NCP; ++c) {
+              if ((c * (KK - 1) * NMF) / NCP == kk * NMF + q && more2) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue1(t + 2, SI{}, c);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         } else {
 #pragma unroll
