@@ -906,6 +906,7 @@ struct StreamKPlan {
   int rem;        // tiles left for the split phase
   int S;          // partial slots per split tile
   float* part;    // [rem][S][BM * BN]
+  bool wide;      // 256 x 320 tiles in a single round (R = 1, rem = 0)
 };
 
 __host__ __device__ inline long sk_units_begin(const StreamKPlan& k, int b) {
@@ -954,6 +955,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_streamk(GemmGroup g, StreamKP
     block_barrier();
     u += k1 - k0;
   }
+}
+
+// Grouped problems in one round of whole tiles, one tile per block.
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int BM, int BN, int NW, int WGM, int F8 = 0>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_group_dp(GemmGroup g) {
+  int q, tm, tn;
+  group_tile<BM, BN>(g, blockIdx.x, q, tm, tn);
+  gemm_tile<A_KMAJ, B_KMAJ, EPI, BM, BN, NW, WGM, F8>(g.p[q], tm, tn, 0, g.p[q].K, nullptr);
 }
 
 // Adds the partial slots of each split-phase tile in piece order (fixed
@@ -1345,10 +1354,14 @@ hipError_t launch_gemm_fp8(const GemmDesc& d, int mode, void* ws, hipStream_t s)
   return e;
 }
 
-// Stream-K plan of a weight-gradient group: 256 x 256 tiles over
-// SK_BLOCKS blocks (the CU count of an MI355X).  Returns false when the
-// problems do not qualify (bf16 MFMA operands, both k-major, fp32 output,
-// one K that is a multiple of BK).
+// Plan of a weight-gradient group.  When the group's 256 x 320 tiles
+// fit one round of SK_BLOCKS blocks (the CU count of an MI355X) and fill at
+// least 7/8 of it, one block per whole tile (plan.wide): no split phase, no
+// partials, no fixup, and 10% fewer operand bytes per FLOP than 256 x 256
+// (d20: 240 tiles, 318 against 335 us for the 256 x 256 stream-K launch with
+// its fixup).  Otherwise stream-K over 256 x 256 tiles.  Returns false when
+// the problems do not qualify (bf16 MFMA operands, both k-major, fp32
+// output, one K that is a multiple of BK).
 constexpr int SK_BLOCKS = 256;
 // fp8: FP8 codes (dY in E5M2 times X in E4M3, both with k = tokens
 // contiguous, launch_gemm_fp8's operand rules), in 128-element k units;
@@ -1358,6 +1371,12 @@ static bool streamk_plan(const GemmDesc* d, int n, int dtype, bool fp8, GemmGrou
   if (n <= 0 || n > GEMM_GROUP_MAX || dtype != 1) return false;
   const int K = d[0].K;
   if (K <= 0 || K % (fp8 ? 16 : BK)) return false;
+  bool wide = true;
+  {
+    long t320 = 0;
+    for (int i = 0; i < n; ++i) t320 += (long)cdiv(d[i].M, 256) * cdiv(d[i].N, 320);
+    if (t320 > SK_BLOCKS || 8 * t320 < 7L * SK_BLOCKS) wide = false;
+  }
   g = GemmGroup{};
   g.count = n;
   int total = 0;
@@ -1375,7 +1394,7 @@ static bool streamk_plan(const GemmDesc* d, int n, int dtype, bool fp8, GemmGrou
     }
     GemmParams p = make_params(d[i]);
     p.tiles_m = cdiv(d[i].M, 256);
-    p.tiles_n = cdiv(d[i].N, 256);
+    p.tiles_n = cdiv(d[i].N, wide ? 320 : 256);
     p.k_split = K;
     p.a_bytes = ab;
     p.b_bytes = bb;
@@ -1385,7 +1404,8 @@ static bool streamk_plan(const GemmDesc* d, int n, int dtype, bool fp8, GemmGrou
   }
   for (int i = n; i <= GEMM_GROUP_MAX; ++i) g.start[i] = total;
   k = StreamKPlan{};
-  k.G = SK_BLOCKS;
+  k.wide = wide;
+  k.G = wide ? total : SK_BLOCKS;
   k.R = total / k.G;
   k.rem = total % k.G;
   k.ku = fp8 ? 128 : BK;
@@ -1421,6 +1441,10 @@ size_t gemm_group_fp8_scratch_bytes(const GemmDesc* d, int n) {
 template <bool AK, bool BKm, int F8>
 static hipError_t run_streamk(const GemmGroup& g, StreamKPlan& k, void* ws, hipStream_t s) {
   k.part = static_cast<float*>(ws);
+  if (k.wide) {
+    hipLaunchKernelGGL((gemm_group_dp<AK, BKm, EPI_F32, 256, 320, 8, 4, F8>), dim3(k.G), dim3(512), 0, s, g);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((gemm_streamk<AK, BKm, EPI_F32, 256, 256, 8, 2, F8>), dim3(k.G), dim3(512), 0, s, g, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.rem == 0) return e;
