@@ -9,7 +9,41 @@ namespace {
 constexpr int ROWS_PER_BLOCK = 4;  // one row per wave, 4 waves per block
 constexpr int MAX_VPL = 4;         // up to 64 * 8 * 4 = 2048 columns
 
-template <typename T, int KIND, bool ROPE>
+// Eight storage elements of a row as loaded (one 16-byte vector for bf16,
+// two for fp32), converted to fp32 only where used, so a wave keeps several
+// rows' loads in flight in few registers.
+template <typename T>
+struct Raw8 {
+  static constexpr int U = sizeof(T) / 2;
+  uint4 u[U];
+  __device__ __forceinline__ void load(const T* p) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) u[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < U; ++i) u[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void get(float* f) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        f[4 * i] = __uint_as_float(u[i].x); f[4 * i + 1] = __uint_as_float(u[i].y);
+        f[4 * i + 2] = __uint_as_float(u[i].z); f[4 * i + 3] = __uint_as_float(u[i].w);
+      }
+    }
+  }
+};
+
+// VPL = vectors of 8 columns per lane (C <= 512 VPL).
+template <typename T, int KIND, bool ROPE, int VPL>
 __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restrict__ x,
                                                   const T* __restrict__ w, const T* __restrict__ b,
                                                   float eps, T* __restrict__ y, float* __restrict__ stats,
@@ -17,54 +51,50 @@ __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restr
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const T* xr = x + (long)row * C;
-  float v[MAX_VPL][8];
-  float s = 0.0f;
-  if constexpr (ROPE) {
+  Raw8<T> v[VPL];
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
-      const int c = (lane + 64 * i) * 8;
-      if (row < N && c < C) Vec8<T>::load(xr + c, v[i]);
-    }
+  for (int i = 0; i < VPL; ++i) {
+    const int c = (lane + 64 * i) * 8;
+    if (row < N && c < C) v[i].load(xr + c);
+  }
+  if constexpr (ROPE) {
     // the RoPE table while the row's loads are in flight
     const int n = rj.T * rj.half, nthr = gridDim.x * blockDim.x;
     for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += nthr) rj.cs[e] = rope_entry(rj, e);
-    if (row >= N) return;
+  }
+  if (row >= N) return;
+  float s = 0.0f;
+  if constexpr (KIND == 0) {
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int c = (lane + 64 * i) * 8;
       if (c < C) {
+        float f[8];
+        v[i].get(f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += v[i][e];
-      }
-    }
-  } else {
-    if (row >= N) return;
-#pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
-      const int c = (lane + 64 * i) * 8;
-      if (c < C) {
-        Vec8<T>::load(xr + c, v[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += v[i][e];
+        for (int e = 0; e < 8; ++e) s += f[e];
       }
     }
   }
   const float mean = KIND == 0 ? wave_sum(s) / C : 0.0f;
   float s2 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MAX_VPL; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     const int c = (lane + 64 * i) * 8;
     if (c < C) {
+      float f[8];
+      v[i].get(f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { float d = v[i][e] - mean; s2 += d * d; }
+      for (int e = 0; e < 8; ++e) { float d = f[e] - mean; s2 += d * d; }
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(s2) / C + eps);
 #pragma unroll
-  for (int i = 0; i < MAX_VPL; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     const int c = (lane + 64 * i) * 8;
     if (c < C) {
-      float o[8];
+      float f[8], o[8];
+      v[i].get(f);
       float wv[8], bv[8];
       if (KIND == 0) {
         if (w) Vec8<T>::load(w + c, wv); else for (int e = 0; e < 8; ++e) wv[e] = 1.0f;
@@ -72,7 +102,7 @@ __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restr
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float h = (v[i][e] - mean) * rstd;
+        float h = (f[e] - mean) * rstd;
         o[e] = KIND == 0 ? fmaf(h, wv[e], bv[e]) : h;
       }
       Vec8<T>::store(y + (long)row * C + c, o);
@@ -85,8 +115,11 @@ __global__ __launch_bounds__(256) void norm_fwd_k(int N, int C, const T* __restr
 }
 
 // dx = norm backward (+ resid); column partials of dy*xhat (gain) and dy
-// (bias) per block into colpart[0][blk][C], colpart[1][blk][C].
-template <typename T, int KIND, bool COLS>
+// (bias) per block into colpart[0][blk][C], colpart[1][blk][C].  A wave
+// walks rows row, row + stride, ...; the next row's x, dy and resid loads
+// are issued before the current row's reductions, so they are in flight
+// while it computes and stores.
+template <typename T, int KIND, bool COLS, int VPL>
 __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restrict__ x,
                                                   const T* __restrict__ w, const T* __restrict__ dy,
                                                   const T* __restrict__ resid, float eps,
@@ -94,53 +127,72 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
   constexpr bool want_cols = COLS;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  float cw[MAX_VPL][8], cb[MAX_VPL][8];
+  const int stride = gridDim.x * ROWS_PER_BLOCK;
+  float cw[VPL][8], cb[VPL][8];
 #pragma unroll
-  for (int i = 0; i < MAX_VPL; ++i)
+  for (int i = 0; i < VPL; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) { cw[i][e] = 0.0f; cb[i][e] = 0.0f; }
 
-  for (int row = blockIdx.x * ROWS_PER_BLOCK + wave; row < N; row += gridDim.x * ROWS_PER_BLOCK) {
-    const T* xr = x + (long)row * C;
-    const T* gr = dy + (long)row * C;
-    float xv[MAX_VPL][8], g[MAX_VPL][8];
-    float s = 0.0f;
+  Raw8<T> nx[VPL], ng[VPL], nr[VPL];
+  auto fetch = [&](int rw) {
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int c = (lane + 64 * i) * 8;
-      if (c < C) {
-        Vec8<T>::load(xr + c, xv[i]);
-        Vec8<T>::load(gr + c, g[i]);
+      if (rw < N && c < C) {
+        nx[i].load(x + (long)rw * C + c);
+        ng[i].load(dy + (long)rw * C + c);
+        if (resid) nr[i].load(resid + (long)rw * C + c); else nr[i].zero();
+      }
+    }
+  };
+  int row = blockIdx.x * ROWS_PER_BLOCK + wave;
+  fetch(row);
+  for (; row < N; row += stride) {
+    Raw8<T> rx[VPL], rg[VPL], rr[VPL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += xv[i][e];
+    for (int i = 0; i < VPL; ++i) { rx[i] = nx[i]; rg[i] = ng[i]; rr[i] = nr[i]; }
+    fetch(row + stride);
+    float s = 0.0f;
+    if constexpr (KIND == 0) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < C) {
+          float f[8];
+          rx[i].get(f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += f[e];
+        }
       }
     }
     const float mean = KIND == 0 ? wave_sum(s) / C : 0.0f;
     float s2 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int c = (lane + 64 * i) * 8;
       if (c < C) {
+        float f[8];
+        rx[i].get(f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { float d = xv[i][e] - mean; s2 += d * d; }
+        for (int e = 0; e < 8; ++e) { float d = f[e] - mean; s2 += d * d; }
       }
     }
     const float rstd = 1.0f / sqrtf(wave_sum(s2) / C + eps);
-    // xhat in xv; gw = dy * w in place of g after column partials
     float sg = 0.0f, sgx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int c = (lane + 64 * i) * 8;
       if (c < C) {
-        float wv[8];
+        float xv[8], g[8], wv[8];
+        rx[i].get(xv);
+        rg[i].get(g);
         if (KIND == 0 && w) Vec8<T>::load(w + c, wv); else for (int e = 0; e < 8; ++e) wv[e] = 1.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float h = (xv[i][e] - mean) * rstd;
-          xv[i][e] = h;
-          if (want_cols) { cw[i][e] = fmaf(g[i][e], h, cw[i][e]); cb[i][e] += g[i][e]; }
-          const float gw = g[i][e] * wv[e];
-          g[i][e] = gw;
+          const float h = (xv[e] - mean) * rstd;
+          if (want_cols) { cw[i][e] = fmaf(g[e], h, cw[i][e]); cb[i][e] += g[e]; }
+          const float gw = g[e] * wv[e];
           sg += gw;
           sgx = fmaf(gw, h, sgx);
         }
@@ -149,13 +201,19 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
     const float mg = KIND == 0 ? wave_sum(sg) / C : 0.0f;
     const float mgx = wave_sum(sgx) / C;
 #pragma unroll
-    for (int i = 0; i < MAX_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int c = (lane + 64 * i) * 8;
       if (c < C) {
-        float o[8], r[8];
-        if (resid) Vec8<T>::load(resid + (long)row * C + c, r); else for (int e = 0; e < 8; ++e) r[e] = 0.0f;
+        float xv[8], g[8], wv[8], r[8], o[8];
+        rx[i].get(xv);
+        rg[i].get(g);
+        rr[i].get(r);
+        if (KIND == 0 && w) Vec8<T>::load(w + c, wv); else for (int e = 0; e < 8; ++e) wv[e] = 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(rstd, g[i][e] - mg - xv[i][e] * mgx, r[e]);
+        for (int e = 0; e < 8; ++e) {
+          const float h = (xv[e] - mean) * rstd;
+          o[e] = fmaf(rstd, g[e] * wv[e] - mg - h * mgx, r[e]);
+        }
         Vec8<T>::store(dx + (long)row * C + c, o);
       }
     }
@@ -164,7 +222,7 @@ __global__ __launch_bounds__(256) void norm_bwd_k(int N, int C, const T* __restr
   // reduce the 4 waves' column partials through LDS, fixed order
   __shared__ float red[ROWS_PER_BLOCK][2][64 * 8];
 #pragma unroll
-  for (int i = 0; i < MAX_VPL; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     if (i > 0 && 64 * 8 * i >= C) break;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -260,16 +318,21 @@ int norm_bwd_blocks(int N) { return std::max(1, std::min(cdiv(N, ROWS_PER_BLOCK)
 hipError_t launch_norm_fwd(int dtype, int kind, int N, int C, const void* x, const void* w,
                            const void* b, float eps, void* y, float* stats, hipStream_t s, const RopeJob* rope) {
   if (N <= 0) return hipSuccess;
+  if (C <= 0 || C > 64 * 8 * MAX_VPL || C % 8) return hipErrorInvalidValue;
   dim3 grid(cdiv(N, ROWS_PER_BLOCK)), block(256);
   RopeJob rj{};
   const bool r = rope && rope->cs;
   if (r) rj = *rope;
-#define NF(T, K, R) hipLaunchKernelGGL((norm_fwd_k<T, K, R>), grid, block, 0, s, N, C, (const T*)x, \
-                                       (const T*)w, (const T*)b, eps, (T*)y, stats, rj)
-#define NFR(T, K) do { if (r) NF(T, K, true); else NF(T, K, false); } while (0)
+  const int vpl = cdiv(C, 512);
+#define NF(T, K, R, V) hipLaunchKernelGGL((norm_fwd_k<T, K, R, V>), grid, block, 0, s, N, C, (const T*)x, \
+                                          (const T*)w, (const T*)b, eps, (T*)y, stats, rj)
+#define NFV(T, K, R) do { switch (vpl) { case 1: NF(T, K, R, 1); break; case 2: NF(T, K, R, 2); break; \
+                                         case 3: NF(T, K, R, 3); break; default: NF(T, K, R, 4); } } while (0)
+#define NFR(T, K) do { if (r) NFV(T, K, true); else NFV(T, K, false); } while (0)
   if (dtype == 1) { if (kind == 0) NFR(bf16, 0); else NFR(bf16, 1); }
   else { if (kind == 0) NFR(float, 0); else NFR(float, 1); }
 #undef NFR
+#undef NFV
 #undef NF
   return hipGetLastError();
 }
@@ -278,17 +341,22 @@ hipError_t launch_norm_bwd(int dtype, int kind, int N, int C, const void* x, con
                            const void* dy, const void* resid, float eps, void* dx,
                            float* colpart, int want_cols, hipStream_t s) {
   if (N <= 0) return hipSuccess;
+  if (C <= 0 || C > 64 * 8 * MAX_VPL || C % 8) return hipErrorInvalidValue;
   dim3 grid(norm_bwd_blocks(N)), block(256);
-#define NB(T, K, COLS) hipLaunchKernelGGL((norm_bwd_k<T, K, COLS>), grid, block, 0, s, N, C, (const T*)x, \
-                                          (const T*)w, (const T*)dy, (const T*)resid, eps, (T*)dx, colpart)
+  const int vpl = cdiv(C, 512);
+#define NB(T, K, COLS, V) hipLaunchKernelGGL((norm_bwd_k<T, K, COLS, V>), grid, block, 0, s, N, C, (const T*)x, \
+                                             (const T*)w, (const T*)dy, (const T*)resid, eps, (T*)dx, colpart)
+#define NBV(T, K, COLS) do { switch (vpl) { case 1: NB(T, K, COLS, 1); break; case 2: NB(T, K, COLS, 2); break; \
+                                            case 3: NB(T, K, COLS, 3); break; default: NB(T, K, COLS, 4); } } while (0)
   // column partials exist only for LayerNorm's gain and bias
   if (dtype == 1) {
-    if (kind == 0) { if (want_cols) NB(bf16, 0, true); else NB(bf16, 0, false); }
-    else NB(bf16, 1, false);
+    if (kind == 0) { if (want_cols) NBV(bf16, 0, true); else NBV(bf16, 0, false); }
+    else NBV(bf16, 1, false);
   } else {
-    if (kind == 0) { if (want_cols) NB(float, 0, true); else NB(float, 0, false); }
-    else NB(float, 1, false);
+    if (kind == 0) { if (want_cols) NBV(float, 0, true); else NBV(float, 0, false); }
+    else NBV(float, 1, false);
   }
+#undef NBV
 #undef NB
   return hipGetLastError();
 }
