@@ -36,13 +36,13 @@ SITE_KERNEL = {
     "qkv_gemm": (["gemm_mfma<false, false, 6, 256, 256, 8, 2, 0>"], "gemm"),
     "fc_gemm_gelu": (["gemm_mfma<false, false, 1, 256, 320, 8, 4, 0>"], "gemm"),
     "proj_dgrad_gelu": (["gemm_mfma<false, true, 2, 256, 320, 8, 4, 0>"], "gemm"),
-    "wgrad_group": (["gemm_streamk<true, true, 3, 256, 256, 8, 2, 0>", "streamk_fixup<256, 256>"], "gemm"),
+    "wgrad_group": (["gemm_group_dp<true, true, 3, 256, 320, 8, 4, 0>"], "gemm"),
     # rocprofv3 prints the bf16 instances of the norm kernels this way
-    "norm1_fwd": (["norm_fwd_k<bool _Accum, int, E, true>"], "norm"),
-    "norm2_fwd": (["norm_fwd_k<bool _Accum, int, E, false>"], "norm"),
+    "norm1_fwd": (["norm_fwd_k<bool _Accum, int, E, true, 3>"], "norm"),
+    "norm2_fwd": (["norm_fwd_k<bool _Accum, int, E, false, 3>"], "norm"),
     # the two backward norms are one instance at one shape
-    "norm1_bwd": (["norm_bwd_k<bool _Accum, int, E, false>"], "norm"),
-    "norm2_bwd": (["norm_bwd_k<bool _Accum, int, E, false>"], "norm"),
+    "norm1_bwd": (["norm_bwd_k<bool _Accum, int, E, false, 3>"], "norm"),
+    "norm2_bwd": (["norm_bwd_k<bool _Accum, int, E, false, 3>"], "norm"),
 }
 SOURCES = {"attention": ["attention.hip", "common.h", "kernels.h"], "gemm": ["gemm.hip", "common.h", "kernels.h"],
            "xent": ["xent.hip", "common.h", "kernels.h"], "norm": ["norm.hip", "common.h", "kernels.h"]}
