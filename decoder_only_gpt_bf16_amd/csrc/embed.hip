@@ -5,15 +5,16 @@
 // wavefront per token row with 16-byte loads.
 //
 // Backward: dwte[v] = sum of dx0 rows whose id is v, in a fixed order, with
-// no floating-point atomics.  The (id, position) pairs are sorted with a
-// stable radix sort (ids are skewed, e.g. Zipf: a few ids own thousands of
-// rows), the sorted list is cut into chunks of CHUNK entries, and one wave
-// per chunk sums each run of equal ids in position order.  A run wholly
-// inside a chunk is written directly; a run crossing chunk boundaries
-// leaves its pieces in per-chunk slots that a second kernel adds in chunk
-// order.  dwpe[t] = sum over the batch of dx0[b, t].
-#include <hipcub/hipcub.hpp>
-
+// no floating-point atomics.  The (id, position) pairs are sorted as 64-bit
+// keys id << 32 | position (all distinct, so the order is by id, then by
+// position) with a bitonic network: tiles of SORT_TILE keys sort in LDS, and
+// merge stages with strides of a tile or more run as passes over global
+// memory.  Ids are skewed (e.g. Zipf: a few ids own thousands of rows); the
+// sorted list is cut into chunks of CHUNK entries, and one wave per chunk
+// sums each run of equal ids in position order.  A run wholly inside a chunk
+// is written directly; a run crossing chunk boundaries leaves its pieces in
+// per-chunk slots that a second kernel adds in chunk order.
+// dwpe[t] = sum over the batch of dx0[b, t].
 #include "kernels.h"
 
 namespace {
@@ -42,15 +43,78 @@ __global__ __launch_bounds__(256) void embed_fwd_k(int N, int TT, int C, int V, 
   }
 }
 
-// Sort keys: the id, or V for an id outside [0, V) (its run is then skipped);
-// values: positions.
-__global__ void keys_k(int N, int V, const int32_t* __restrict__ ids, int32_t* __restrict__ keys,
-                       int32_t* __restrict__ vals) {
+// Sort keys: (id, or V for an id outside [0, V), whose run is then skipped)
+// << 32 | position, padded to P (a power of two) with all-ones keys that sort
+// last.
+__global__ void sort_keys_k(int N, int P, int V, const int32_t* __restrict__ ids, uint64_t* __restrict__ k) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P) return;
+  if (i < N) {
+    const int id = ids[i];
+    const uint32_t key = (id >= 0 && id < V) ? (uint32_t)id : (uint32_t)V;
+    k[i] = ((uint64_t)key << 32) | (uint32_t)i;
+  } else {
+    k[i] = ~0ull;
+  }
+}
+
+// Bitonic network, ascending over P = 2^p keys: in merge m (2, 4, .., P)
+// the stage of stride s (m / 2, .., 1) orders each pair (i, i + s) with
+// i & s == 0, ascending when i & m == 0 and descending otherwise.
+constexpr int SORT_TILE = 8192;  // keys per LDS tile (64 KB)
+constexpr int SORT_THREADS = 1024;
+
+__device__ __forceinline__ void cmp_swap(uint64_t& a, uint64_t& b, bool up) {
+  if ((a > b) == up) {
+    const uint64_t t = a;
+    a = b;
+    b = t;
+  }
+}
+
+// One block per tile of n = min(P, SORT_TILE) keys: the merges m_lo .. m_hi
+// (powers of two), each from stride min(m / 2, n / 2) down to 1, in LDS.
+// The initial sort takes m_lo = 2, m_hi = n; a merge m > n takes
+// m_lo = m_hi = m after its global stages.
+__global__ __launch_bounds__(SORT_THREADS) void bitonic_tile_k(uint64_t* __restrict__ k, int n, int m_lo,
+                                                               int m_hi) {
+  __shared__ uint64_t t[SORT_TILE];
+  const long base = (long)blockIdx.x * n;
+  for (int i = threadIdx.x; i < n; i += SORT_THREADS) t[i] = k[base + i];
+  __syncthreads();
+  for (int m = m_lo; m <= m_hi; m <<= 1) {
+    for (int s = min(m, n) >> 1; s > 0; s >>= 1) {
+      for (int q = threadIdx.x; q < n / 2; q += SORT_THREADS) {
+        const int i = (q / s) * 2 * s + (q % s);  // lower element of the pair
+        const bool up = ((base + i) & m) == 0;
+        cmp_swap(t[i], t[i + s], up);
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += SORT_THREADS) k[base + i] = t[i];
+}
+
+// One stage (merge m, stride s >= the tile size) over global memory: one
+// thread per pair.
+__global__ __launch_bounds__(256) void bitonic_pass_k(uint64_t* __restrict__ k, long P, long m, long s) {
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= P / 2) return;
+  const long i = (q / s) * 2 * s + (q % s);
+  uint64_t a = k[i], b = k[i + s];
+  cmp_swap(a, b, (i & m) == 0);
+  k[i] = a;
+  k[i + s] = b;
+}
+
+// Split the sorted keys into ids and positions (first N entries).
+__global__ void split_keys_k(int N, const uint64_t* __restrict__ k, int32_t* __restrict__ skeys,
+                             int32_t* __restrict__ spos) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
-  const int id = ids[i];
-  keys[i] = (id >= 0 && id < V) ? id : V;
-  vals[i] = i;
+  const uint64_t v = k[i];
+  skeys[i] = (int32_t)(v >> 32);
+  spos[i] = (int32_t)(v & 0xffffffffu);
 }
 
 __global__ void fill_i32_k(long n, int32_t* p, int32_t v) {
@@ -185,33 +249,36 @@ __global__ __launch_bounds__(256) void embed_pos_k(int B, int TT, int C, int row
 }
 
 struct EmbedWs {
-  size_t keys, keys_out, vals, vals_out, seg_start, seg_end, slots, cub, total;
-  size_t cub_bytes;
+  size_t sort, skeys, spos, seg_start, seg_end, slots, total;
+  long P;  // keys sorted: N rounded up to a power of two
 };
 
 EmbedWs embed_ws_layout(int N, int V, int C) {
   EmbedWs w{};
-  size_t cub = 0;
-  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cub, (const uint32_t*)nullptr, (uint32_t*)nullptr,
-                                           (const int32_t*)nullptr, (int32_t*)nullptr, N, 0, 32, (hipStream_t)0);
+  w.P = 2;
+  while (w.P < N) w.P <<= 1;
   size_t o = 0;
-  w.keys = o; o += align256((size_t)N * 4);
-  w.keys_out = o; o += align256((size_t)N * 4);
-  w.vals = o; o += align256((size_t)N * 4);
-  w.vals_out = o; o += align256((size_t)N * 4);
+  w.sort = o; o += align256((size_t)w.P * 8);
+  w.skeys = o; o += align256((size_t)N * 4);
+  w.spos = o; o += align256((size_t)N * 4);
   w.seg_start = o; o += align256((size_t)V * 4);
   w.seg_end = o; o += align256((size_t)V * 4);
   w.slots = o; o += align256((size_t)2 * cdiv(N, CHUNK) * C * 4);
-  w.cub = o; o += align256(cub);
-  w.cub_bytes = cub;
   w.total = o;
   return w;
 }
 
-int end_bit_for(int V) {
-  int b = 1;
-  while ((1L << b) < V) ++b;
-  return b;
+// Sorts the P keys at k ascending (the bitonic network above).
+hipError_t bitonic_sort(uint64_t* k, long P, hipStream_t s) {
+  const int n = (int)std::min<long>(P, SORT_TILE);
+  const unsigned tiles = (unsigned)(P / n);
+  hipLaunchKernelGGL(bitonic_tile_k, dim3(tiles), dim3(SORT_THREADS), 0, s, k, n, 2, n);
+  for (long m = 2L * n; m <= P; m <<= 1) {
+    for (long st = m >> 1; st >= n; st >>= 1)
+      hipLaunchKernelGGL(bitonic_pass_k, dim3((unsigned)cdiv(P / 2, 256)), dim3(256), 0, s, k, P, m, st);
+    hipLaunchKernelGGL(bitonic_tile_k, dim3(tiles), dim3(SORT_THREADS), 0, s, k, n, (int)m, (int)m);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -241,21 +308,18 @@ hipError_t launch_embed_bwd(int dtype, int B, int T, int C, int V, int wpe_rows,
   EmbedWs w = embed_ws_layout(N, V, C);
   if (scratch_bytes < w.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(scratch);
-  int32_t* keys = reinterpret_cast<int32_t*>(base + w.keys);
-  int32_t* keys_out = reinterpret_cast<int32_t*>(base + w.keys_out);
-  int32_t* vals = reinterpret_cast<int32_t*>(base + w.vals);
-  int32_t* vals_out = reinterpret_cast<int32_t*>(base + w.vals_out);
+  uint64_t* sortk = reinterpret_cast<uint64_t*>(base + w.sort);
+  int32_t* keys_out = reinterpret_cast<int32_t*>(base + w.skeys);
+  int32_t* vals_out = reinterpret_cast<int32_t*>(base + w.spos);
   int32_t* seg_start = reinterpret_cast<int32_t*>(base + w.seg_start);
   int32_t* seg_end = reinterpret_cast<int32_t*>(base + w.seg_end);
   float* slots = reinterpret_cast<float*>(base + w.slots);
-  hipLaunchKernelGGL(keys_k, dim3(cdiv(N, 256)), dim3(256), 0, s, N, V, ids, keys, vals);
+  hipLaunchKernelGGL(sort_keys_k, dim3((unsigned)cdiv(w.P, 256)), dim3(256), 0, s, N, (int)w.P, V, ids, sortk);
   hipLaunchKernelGGL(fill_i32_k, dim3(std::min(cdiv(V, 256), 1024)), dim3(256), 0, s, (long)V, seg_start, -1);
   hipLaunchKernelGGL(fill_i32_k, dim3(std::min(cdiv(V, 256), 1024)), dim3(256), 0, s, (long)V, seg_end, -1);
-  size_t cub = w.cub_bytes;
-  hipError_t e = hipcub::DeviceRadixSort::SortPairs(base + w.cub, cub, reinterpret_cast<const uint32_t*>(keys),
-                                                    reinterpret_cast<uint32_t*>(keys_out), vals, vals_out, N, 0,
-                                                    end_bit_for(V + 1), s);
+  hipError_t e = bitonic_sort(sortk, w.P, s);
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_keys_k, dim3(cdiv(N, 256)), dim3(256), 0, s, N, sortk, keys_out, vals_out);
   hipLaunchKernelGGL(seg_bounds_k, dim3(cdiv(N, 256)), dim3(256), 0, s, N, V, keys_out, seg_start, seg_end);
   const int nchunk = cdiv(N, CHUNK);
   if (dtype == 1)

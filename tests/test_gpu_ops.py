@@ -201,6 +201,35 @@ def test_embed_fwd_bwd(dtype, rope, zipf):
     torch.testing.assert_close(dwte, 2 * d1, rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("T", [5000, 20000])
+def test_embed_bwd_multi_tile_sort(T):
+    """The (id, position) sort across several 8192-key tiles: 10000 tokens
+    sort as 16384 keys (one merge over global memory), 40000 as 65536 keys
+    (three merges, six global stages); Zipf ids, so long runs of one id cross
+    tile and chunk boundaries.  The sums must equal the oracle's, untouched
+    rows stay zero, and a second call with accumulate adds the identical
+    result."""
+    print_case("embed-multi-tile", T)
+    rng = np.random.default_rng(11)
+    Bsz, C, V = 2, 64, 50304
+    cfg = synth.GPTConfig(n_layer=1, n_head=2, n_embd=C, block_size=T, vocab_size=V, rope=True, dtype="bf16")
+    c = B.make_config(cfg)
+    ids = synth.zipf_ids(rng, (Bsz, T), 50257, 1.1)
+    dx0 = synth.round_to(rng.standard_normal((Bsz, T, C)), "bf16")
+    ws = workspace(c, Bsz, T)
+    dwte = torch.full((V, C), 3.0, dtype=torch.float32, device="cuda")
+    B.gpt_embed_bwd(c, Bsz, T, upload_i32(ids), upload(dx0.reshape(-1, C), "bf16"), dwte, None, 0, ws)
+    torch.cuda.synchronize()
+    ref, _ = O.embed_bwd(dx0, ids, V, 0)
+    assert_rel("dwte", to_f64(dwte), ref, 1e-5)
+    untouched = np.setdiff1d(np.arange(V), ids.reshape(-1))
+    assert not to_f64(dwte)[untouched].any()
+    d1 = dwte.clone()
+    B.gpt_embed_bwd(c, Bsz, T, upload_i32(ids), upload(dx0.reshape(-1, C), "bf16"), dwte, None, 1, ws)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(dwte, 2 * d1, rtol=0, atol=0)
+
+
 def test_embed_out_of_range_ids():
     """ids outside [0, V) embed to zero and contribute no gradient."""
     Bsz, T, C, V = 1, 40, 64, 100
