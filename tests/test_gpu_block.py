@@ -170,9 +170,10 @@ def test_block_inference_matches_training_forward():
     assert torch.equal(y1, r.y)
 
 
-# Shapes whose grouped weight-gradient launch leaves some of its 256 blocks
-# without k-steps in the split phase (tiles left over x k-steps < 256): d20
-# at 128..320 tokens (44 leftover tiles), GPT-2 at 128 tokens (108 tiles).
+# Small token counts for the grouped weight-gradient launch: at the GPT-2
+# width (108 tiles of 256 x 256, stream-K) 128 tokens leave some of the 256
+# blocks without k-steps in the split phase; the d20 width takes one round of
+# 240 tiles of 256 x 320 at any token count.
 STREAMK_SPARSE = [("d20_block", 1, 128), ("d20_block", 1, 192), ("d20_block", 1, 320), ("gpt2_block", 1, 128)]
 
 
@@ -201,11 +202,13 @@ def test_block_parity_stale_workspace(name, Bsz, T):
 
 
 @pytest.mark.parametrize("name,Bsz,T,fp8", [("d20_block", 1, 192, False), ("d20_block", 2, 2048, False),
-                                             ("d20_block", 2, 2048, True)])
+                                             ("d20_block", 2, 2048, True), ("gpt2_block", 1, 128, False),
+                                             ("gpt2_block", 8, 1024, False)])
 def test_block_accumulate_streamk(name, Bsz, T, fp8):
-    """accumulate=1 through the grouped stream-K weight gradients (both the
-    whole tiles' epilogue and the fixup of the split tiles; bf16, or FP8
-    codes with fp8): a second identical backward doubles every parameter
+    """accumulate=1 through the grouped weight gradients: the d20 width's
+    single round of 256 x 320 tiles (bf16, or FP8 codes with fp8) and the
+    GPT-2 width's stream-K launch (the whole tiles' epilogue and the fixup of
+    the split tiles).  A second identical backward doubles every parameter
     gradient exactly (the reductions have a fixed order, so the two passes
     are bitwise equal)."""
     w = synth.scaled(synth.BY_NAME[name], B=Bsz, T=T, fp8=fp8)
