@@ -39,6 +39,10 @@ CASES = [
     # k-tile counts 10, 30 and 40 (all three remainders of the loop's
     # unrolling by three)
     ("d20_block", dict(B=8, T=2048, n_embd=640, n_head=5), False),
+    # the d20 form at C = 1216 (19 heads of 64): the four weight gradients
+    # take the single round of 256 x 320 tiles (236 of them), ragged in both
+    # dimensions (1216 = 4 x 256 + 192 rows, 3648 = 11 x 320 + 128 columns)
+    ("d20_block", dict(B=2, T=300, n_embd=1216, n_head=19), False),
 ]
 
 

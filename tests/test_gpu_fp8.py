@@ -124,11 +124,13 @@ def test_fp8_linear_end_to_end():
 
 # ---- the block with FP8 Linear layers (gpt_config.fp8) against the oracle's
 # FP8 block ----
+# (C = 1216: the FP8 weight gradients' single round of 256 x 320 tiles,
+# ragged in both dimensions)
 FP8_BLOCK = [("d20_block", dict(B=2, T=200)), ("gpt2_block", dict(B=2, T=200)), ("d20_block", dict(B=1, T=77)),
-             ("d20_block", dict()), ("gpt2_block", dict())]
+             ("d20_block", dict()), ("gpt2_block", dict()), ("d20_block", dict(B=2, T=300, n_embd=1216, n_head=19))]
 
 
-@pytest.mark.parametrize("name,sz", FP8_BLOCK, ids=[f"{n}-{s.get('B', 'full')}-{s.get('T', 'full')}" for n, s in FP8_BLOCK])
+@pytest.mark.parametrize("name,sz", FP8_BLOCK, ids=[f"{n}-{s.get('B', 'full')}-{s.get('T', 'full')}-C{s.get('n_embd', 'std')}" for n, s in FP8_BLOCK])
 def test_fp8_block_parity(name, sz):
     w = synth.scaled(synth.BY_NAME[name], fp8=True, **sz)
     print_case("fp8-block", name, w.B, w.T)
