@@ -199,12 +199,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int swzq(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 //   k-major tiles, 320-byte rows (20 units): f(r) = (r >> 2) & 3 (stays in range)
+//   k-major tiles, 384-byte rows (24 units): f(r) = ((r >> 1) & 1) << 2 (below 8,
+//     so it stays in range; the row stride is 32 banks mod 64, and within
+//     each aligned group of four k-rows the two even and the two odd rows
+//     take opposite halves of their 32 banks)
 //   k-major tiles, 640-byte rows (40 units): f(r) = tab[r & 15] < 8, found by
 //   search over such tables
 template <int UPR>
 __device__ __forceinline__ int swz_km(int r) {
   if constexpr (UPR == 20) {
     return (r >> 2) & 3;
+  } else if constexpr (UPR == 24) {
+    return ((r >> 1) & 1) << 2;
   } else if constexpr (UPR == 40) {
     constexpr uint64_t tab = 0x6433054362356005ull;  // nibble i = f(i): 5,0,0,6,5,3,2,6,3,4,5,0,3,3,4,6
     return (int)((tab >> (4 * (r & 15))) & 0xf);
@@ -1073,13 +1079,15 @@ Plan plan_mfma(const GemmDesc& d) {
   // whole rounds of the 256 CUs: 256 x 320 when it fills them exactly and
   // 256 x 256 would leave a partial round (e.g. N = 5120, M = 8192)
   const bool r320 = d.N % 320 == 0 && t320 >= 256 && t320 % 256 == 0 && t256 % 256 != 0;
-  // 256 x 192 (k-contiguous bf16 operands, store and GELU epilogues) where
-  // it fills the CUs in whole rounds and 256 x 256 would not: the GPT-2
-  // width's N = 3072 at M = 8192 and N = 768 at M = 16384 (a 128 x 192 tile
-  // for N = 768 at M = 8192 measured no faster than 128 x 128)
-  const bool r192 = d.N % 192 == 0 && !d.a_kmaj && !d.b_kmaj && !d.f8_sa &&
-                    (d.epi == EPI_STORE || d.epi == EPI_GELU) && (long)cdiv(d.M, 256) * (d.N / 192) % 256 == 0 &&
-                    t256 % 256 != 0;
+  // 256 x 192 (bf16, A k-contiguous, B either way; store, GELU, GELU' and
+  // fp32 epilogues) where it fills the CUs in whole rounds and 256 x 256
+  // would not: the GPT-2 width's N = 3072 at M = 8192 (FC forward, proj
+  // input gradient) and N = 768 at M = 16384 (the LM head's input gradient
+  // among them; a 128 x 192 tile for N = 768 at M = 8192 measured no faster
+  // than 128 x 128)
+  const bool r192 = d.N % 192 == 0 && !d.a_kmaj && !d.f8_sa &&
+                    (d.epi == EPI_STORE || d.epi == EPI_GELU || d.epi == EPI_GELU_BWD || d.epi == EPI_F32) &&
+                    (long)cdiv(d.M, 256) * (d.N / 192) % 256 == 0 && t256 % 256 != 0;
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
   else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
   else if (r192) { pl.BMv = 256; pl.BNv = 192; }
@@ -1134,7 +1142,7 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
   }
   if (pl.BNv == 192) {
     // 8 waves of 64 x 96
-    if constexpr (F8 == 0 && !AK && !BKm && (EPI == EPI_STORE || EPI == EPI_GELU)) {
+    if constexpr (F8 == 0 && !AK && (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_GELU_BWD || EPI == EPI_F32)) {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
       hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 192, 8, 4, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
