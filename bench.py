@@ -53,7 +53,7 @@ HEAD_PROFILES = {name: os.path.join(HERE, "profiles", f"hbm_traffic_{name}.md")
 HEAD_SITE_KERNEL = {
     "xent_stats_gemm": (["gemm_mfma<false, false, 4, 256, 256, 8, 2, 0>"], "gemm"),
     "xent_grad_gemm": (["gemm_mfma<false, false, 5, 256, 256, 8, 2, 0>"], "gemm"),
-    "xent_dh_gemm": (["gemm_mfma<false, true, 3, 128, 128, 4, 2, 0>"], "gemm"),
+    "xent_dh_gemm": (["gemm_mfma<false, true, 3, 256, 192, 8, 4, 0>"], "gemm"),
     "xent_finish": (["xent_finish_k"], "xent"),
     "xent_dh_convert": (["_ZN12_GLOBAL__N_18f32_to_kIDF16bEEvlPKfPT_"], "xent"),
 }
