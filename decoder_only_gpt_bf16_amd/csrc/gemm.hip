@@ -1085,12 +1085,18 @@ Plan plan_mfma(const GemmDesc& d) {
   // input gradient) and N = 768 at M = 16384 (the LM head's input gradient
   // among them; a 128 x 192 tile for N = 768 at M = 8192 measured no faster
   // than 128 x 128)
-  const bool r192 = d.N % 192 == 0 && !d.a_kmaj && !d.f8_sa &&
+  const long t192 = d.N % 192 == 0 ? (long)cdiv(d.M, 256) * (d.N / 192) : 0;
+  const bool r192 = t192 > 0 && !d.a_kmaj && !d.f8_sa &&
                     (d.epi == EPI_STORE || d.epi == EPI_GELU || d.epi == EPI_GELU_BWD || d.epi == EPI_F32) &&
-                    (long)cdiv(d.M, 256) * (d.N / 192) % 256 == 0 && t256 % 256 != 0;
+                    t192 % 256 == 0 && t256 % 256 != 0;
+  // fp32-output products with both operands k-major (weight-gradient form,
+  // long K): 256 x 192 when the tiles, split along K, fill the 256 CUs
+  // exactly (the GPT-2 LM head's dW: 128 tiles, two K halves)
+  const bool k192 = t192 > 0 && d.a_kmaj && d.b_kmaj && !d.f8_sa && d.epi == EPI_F32 && 256 % t192 == 0 &&
+                    d.K / (256 / t192) >= 1024;
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
   else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
-  else if (r192) { pl.BMv = 256; pl.BNv = 192; }
+  else if (r192 || k192) { pl.BMv = 256; pl.BNv = 192; }
   else if (t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
   else if (d.N % 160 == 0 && t160 >= 240 && t160 % 256 <= 16) { pl.BMv = 256; pl.BNv = 160; }
   else { pl.BMv = 128; pl.BNv = 128; }
@@ -1142,7 +1148,8 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
   }
   if (pl.BNv == 192) {
     // 8 waves of 64 x 96
-    if constexpr (F8 == 0 && !AK && (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_GELU_BWD || EPI == EPI_F32)) {
+    if constexpr (F8 == 0 && (AK ? (BKm && EPI == EPI_F32)
+                                 : (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_GELU_BWD || EPI == EPI_F32))) {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
       hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 192, 8, 4, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
