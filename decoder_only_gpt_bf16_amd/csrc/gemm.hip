@@ -405,9 +405,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tm, int tn, i
   // the whole tile, double-buffered, with rows padded to QKP floats
   constexpr int QKP = 260;
   constexpr int QK_UNITS = EPI == EPI_QKNORM ? 2 * 64 * QKP / 4 : 0;
-  // 256 x 160 bf16 tiles keep three k-tile stages (156 KB), so that two
-  // tiles' copies are in flight while the MFMAs run; the others keep two
-  constexpr bool PIPE3 = F8 == 0 && NW == 8 && BM == 256 && BN == 160;
+  // 256 x 160 and 256 x 96 bf16 tiles keep three k-tile stages (156 and
+  // 135 KB), so that two tiles' copies are in flight while the MFMAs run;
+  // the others keep two
+  constexpr bool PIPE3 = F8 == 0 && NW == 8 && BM == 256 && (BN == 160 || BN == 96);
   constexpr int NSTAGE = PIPE3 ? 3 : 2;
   constexpr int LDS_UNITS0 = NSTAGE * STAGE_UNITS > EPI_UNITS ? NSTAGE * STAGE_UNITS : EPI_UNITS;
   __shared__ uint4 lds[LDS_UNITS0 > QK_UNITS ? LDS_UNITS0 : QK_UNITS];
@@ -1094,7 +1095,13 @@ Plan plan_mfma(const GemmDesc& d) {
   // exactly (the GPT-2 LM head's dW: 128 tiles, two K halves)
   const bool k192 = t192 > 0 && d.a_kmaj && d.b_kmaj && !d.f8_sa && d.epi == EPI_F32 && 256 % t192 == 0 &&
                     d.K / (256 / t192) >= 1024;
+  // 256 x 96 (8 waves of 32 x 96, k-contiguous bf16, store epilogue) where
+  // it fills the CUs in exactly one round and neither 256 x 256 nor
+  // 256 x 192 would: the GPT-2 width's N = 768 products at M = 8192
+  const bool r96 = d.N % 96 == 0 && !d.a_kmaj && !d.b_kmaj && !d.f8_sa && d.epi == EPI_STORE &&
+                   (long)cdiv(d.M, 256) * (d.N / 96) == 256 && t256 < 240 && !(t192 > 0 && t192 % 256 == 0);
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
+  else if (r96) { pl.BMv = 256; pl.BNv = 96; }
   else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
   else if (r192 || k192) { pl.BMv = 256; pl.BNv = 192; }
   else if (t256 >= 240) { pl.BMv = 256; pl.BNv = 256; }
@@ -1152,6 +1159,16 @@ hipError_t go_mfma_tiles(const GemmParams& p, const Plan& pl, hipStream_t s) {
                                  : (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_GELU_BWD || EPI == EPI_F32))) {
       dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
       hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 192, 8, 4, F8>), grid, dim3(512), 0, s, p);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (pl.BNv == 96) {
+    // 8 waves of 32 x 96
+    if constexpr (F8 == 0 && !AK && !BKm && EPI == EPI_STORE) {
+      dim3 grid(p.tiles_m * p.tiles_n, 1, pl.splits);
+      hipLaunchKernelGGL((gemm_mfma<AK, BKm, EPI, 256, 96, 8, 8, F8>), grid, dim3(512), 0, s, p);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;
