@@ -1096,10 +1096,12 @@ Plan plan_mfma(const GemmDesc& d) {
   const bool k192 = t192 > 0 && d.a_kmaj && d.b_kmaj && !d.f8_sa && d.epi == EPI_F32 && 256 % t192 == 0 &&
                     d.K / (256 / t192) >= 1024;
   // 256 x 96 (8 waves of 32 x 96, k-contiguous bf16, store epilogue) where
-  // it fills the CUs in exactly one round and neither 256 x 256 nor
-  // 256 x 192 would: the GPT-2 width's N = 768 products at M = 8192
+  // it fills the CUs in whole rounds and neither 256 x 256 nor 256 x 192
+  // would: at the GPT-2 width and M = 8192, the N = 768 products (one round)
+  // and the QKV forward (N = 2304: three rounds, against 1.125 of 256 x 256)
   const bool r96 = d.N % 96 == 0 && !d.a_kmaj && !d.b_kmaj && !d.f8_sa && d.epi == EPI_STORE &&
-                   (long)cdiv(d.M, 256) * (d.N / 96) == 256 && t256 < 240 && !(t192 > 0 && t192 % 256 == 0);
+                   (long)cdiv(d.M, 256) * (d.N / 96) % 256 == 0 && t256 % 256 != 0 &&
+                   !(t192 > 0 && t192 % 256 == 0);
   if (d.epi == EPI_XENT_STATS || d.epi == EPI_QKNORM) { pl.BMv = 256; pl.BNv = 256; }
   else if (r96) { pl.BMv = 256; pl.BNv = 96; }
   else if (r320 && d.epi != EPI_F32) { pl.BMv = 256; pl.BNv = 320; }
